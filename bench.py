@@ -1,0 +1,258 @@
+"""Throughput of the KV-cached attention step on one MI355X.
+
+A step is one pass of the whole path over one batch: append the T new K/V
+rows of every sequence (kvc_append), then attend the new queries over the
+cache (kvc_attn_decode / kvc_attn_verify; the launch plan is host-side
+inside the call). Inputs are seeded synthetic draws already resident in HBM.
+
+value = algorithmic KV bytes per step / step time, in GB/s, where the
+algorithmic bytes are the K and V rows each step must read:
+sum_b seq_len_b * 2 * K * H * elem_bytes. The default workload is batched
+decode (B=64, N=32, K=8, H=128, bf16, T=1, cached context U[512, 4096]).
+
+Prints ONE JSON line. ``--gpus`` above 1 is refused: this path runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV read GB/s (% of ~8 TB/s HBM peak); tokens/s per step"
+HBM_PEAK_GBS = 8000.0
+# Infinity Cache (MALL) on MI355X; cache replicas are rotated so that each
+# step's reads exceed it at least twice over.
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="batched_decode_b64")
+    p.add_argument("--ctx", type=int, default=4096, help="cached context for layers24_b1_sweep")
+    p.add_argument("--num-workgroups", type=int, default=0)
+    p.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough to defeat the MALL)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Step:
+    """Everything one replica of the workload needs on the GPU."""
+
+    def __init__(self, w, prior, seed, dev, nwg, layer=None):
+        import torch
+
+        import kv_cached_gqa_attention_amd as kvc
+        from workloads import draw_inputs, layout_contiguous, layout_paged, make_block_table
+
+        self.kvc = kvc
+        self.w = w
+        self.inp = draw_inputs(w.B, w.T, w.N, w.K, w.H, w.dtype, prior, seed, device=dev)
+        if w.layout == "paged":
+            table, nb = make_block_table(seed + 7, self.inp.seq_lens, w.block_size)
+            pk, pv = layout_paged(self.inp, table, nb, w.block_size, pad_value=0.0)
+            self.cache = kvc.Cache(pk, pv, torch.from_numpy(table).to(dev))
+        else:
+            ck, cv = layout_contiguous(self.inp, pad_value=0.0)
+            self.cache = kvc.Cache(ck, cv)
+        # the draws' context rows are no longer needed on the device
+        self.inp.ctx_k = self.inp.ctx_k[:0]
+        self.inp.ctx_v = self.inp.ctx_v[:0]
+        self.seq_lens = torch.from_numpy(self.inp.seq_lens.astype(np.int32)).to(dev)
+        self.max_len = int(self.inp.seq_lens.max())
+        self.q = self.inp.q[:, 0].contiguous() if w.T == 1 else self.inp.q
+        self.out = torch.empty(self.q.shape, dtype=w.dtype, device=dev)
+        self.nwg = nwg
+        need = kvc.workspace_bytes(w.B, w.T, w.N, w.K, w.H, self.max_len, nwg)
+        self.ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+
+    def append(self):
+        self.kvc.append(self.cache, self.inp.k_new, self.inp.v_new, self.seq_lens)
+
+    def attend(self):
+        f = self.kvc.decode if self.w.T == 1 else self.kvc.verify
+        f(self.q, self.cache, self.seq_lens, self.max_len, out=self.out, out_dtype=self.w.dtype,
+          num_workgroups=self.nwg, ws=self.ws)
+
+
+def kv_bytes(w, seq_lens) -> int:
+    return int(np.sum(seq_lens)) * 2 * w.K * w.H * w.elem_bytes
+
+
+def cpu_baseline(w, prior, seed, budget_s):
+    """Time the CPU oracle on whole (sequence, key-value head) units of the
+    same workload until ``budget_s`` seconds pass; report KV GB/s."""
+    import torch
+
+    from oracle import attend
+    from workloads import draw_inputs, logical_kv
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    scale = 1.0 / math.sqrt(w.H)
+    G = w.N // w.K
+    done_bytes = 0
+    units = 0
+    elapsed = 0.0
+    b = 0
+    while elapsed < budget_s and b < w.B:
+        one = draw_inputs(1, w.T, w.N, w.K, w.H, w.dtype, prior[b : b + 1], seed + 1000 + b, device="cpu")
+        kb, vb = logical_kv(one, 0)
+        for k in range(w.K):
+            kk = kb[:, k : k + 1].double().numpy()
+            vv = vb[:, k : k + 1].double().numpy()
+            q = one.q[:, :, k * G : (k + 1) * G].double().numpy()
+            t0 = time.perf_counter()
+            attend(q, [kk], [vv], scale)
+            elapsed += time.perf_counter() - t0
+            done_bytes += kk.shape[0] * 2 * w.H * w.elem_bytes
+            units += 1
+            if elapsed >= budget_s:
+                break
+        b += 1
+    del torch
+    return {
+        "value": done_bytes / elapsed / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{units} (sequence, kv-head) units of {w.name} (prior context drawn from the same "
+                  f"distribution), fp64 numpy oracle, {elapsed:.1f} s of CPU time; host has "
+                  f"{os.cpu_count()} logical CPUs",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from workloads import draw_prior_lengths, get_workload
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    if w.prior_sweep:
+        prior = np.full(w.B, args.ctx, dtype=np.int64)
+    else:
+        prior = draw_prior_lengths(w.seed, w.B, w.prior_lo, w.prior_hi)
+    seq_lens = prior + w.T
+    step_bytes = kv_bytes(w, seq_lens)
+    layers = w.layers
+    if args.replicas > 0:
+        reps = args.replicas
+    else:
+        reps = max(1, math.ceil(2 * MALL_BYTES / max(1, step_bytes * layers)))
+        reps = min(reps, 4096)
+    log(f"bench: {w.name} ({w.description}); KV bytes/step {step_bytes * layers / 1e6:.1f} MB; "
+        f"{reps} replica(s) x {layers} layer(s)")
+    steps = [[Step(w, prior, w.seed * 1000 + r * layers + l, dev, args.num_workgroups) for l in range(layers)]
+             for r in range(reps)]
+    torch.cuda.synchronize()
+
+    def run_step(i):
+        for s in steps[i % reps]:
+            s.append()
+            s.attend()
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Attention kernel alone: HIP events on the stream the kernel runs on
+    # (torch's current stream is the one handed to the library).
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * layers)]
+    for i in range(args.steps):
+        for l, s in enumerate(steps[i % reps]):
+            s.append()
+            a, b = ev[i * layers + l]
+            a.record(stream)
+            s.attend()
+            b.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    achieved = step_bytes / (attn_ms * 1e-3) / 1e9
+
+    value = step_bytes * layers / (ms_per_step * 1e-3) / 1e9
+    tokens = w.B * w.T
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype_name(),
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "batch": w.B,
+            "query_tokens": w.T,
+            "q_heads": w.N,
+            "kv_heads": w.K,
+            "head_dim": w.H,
+            "layers": layers,
+            "kv_bytes_per_step": step_bytes * layers,
+            "mean_seq_len": float(np.mean(seq_lens)),
+            "replicas": reps,
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
+        "attention_steps_per_s": round(1e3 / ms_per_step, 1),
+        "roofline": {
+            "kernel": "attn_mfma_kernel" if w.G * w.T > 8 else "attn_valu_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launch_ms": round(attn_ms, 5),
+            "bytes_per_launch": step_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, prior, w.seed, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

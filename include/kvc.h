@@ -1,0 +1,193 @@
+/*
+ * kvc.h - attention of a few new query tokens against a growing key/value
+ * cache, with grouped-query heads, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages this follows):
+ *
+ *  - "Making inference cheap: KV cache, batching and quantization": keys and
+ *    values of earlier positions never change once computed (the causal-mask
+ *    paragraph), so they are stored and each generation step attends the new
+ *    token's query over every stored key, one 1 x n score row per head.
+ *  - "CS336, lectures 10 and 12: inference and evaluation", section
+ *    "Arithmetic intensity of inference" (attention layers): A = Q K^T,
+ *    Y = softmax(A) V; section "Reducing the KV cache": N query heads share
+ *    K key-value heads, each serving a group of G = N / K query heads.
+ *  - "Stanford CS336 Day 13 - Inference", "Attention layers": the grouped
+ *    shapes, scores B x S x T x K x G against values B x S x K x H.
+ *  - "Accelerating Sonar through speculation", section "Speculative
+ *    decoding": the target model scores n drafted tokens in one pass, giving
+ *    up to n + 1 tokens; the verify call here is that pass's attention, over
+ *    T = n + 1 query tokens, causal inside the block.
+ *  - "CS336, lectures 10 and 12", section "PagedAttention": the cache of a
+ *    sequence is split into fixed-size blocks (e.g. 16 tokens) and a
+ *    per-sequence block table maps logical blocks to physical ones; blocks
+ *    may be shared between sequences (prefix sharing).
+ *  - "Accelerating Sonar through speculation", section "Inference with
+ *    speculative decoding": batch metadata is copied to GPU memory before
+ *    the model runs, and the accepted length must not force a GPU-to-CPU
+ *    synchronisation; hence lengths and block tables are DEVICE arrays here
+ *    and no call ever reads them on the host.
+ *
+ * Definitions used by every call. Sequence b holds seq_lens[b] valid tokens
+ * AFTER its T new tokens are appended; P_b = seq_lens[b] - T tokens were
+ * cached before. New token t (0 <= t < T) of sequence b is at absolute
+ * position P_b + t and attends keys 0 .. P_b + t. Query head n reads
+ * key-value head n / G (each key-value head serves a contiguous group).
+ *     s_j   = scale * <q, k_j>
+ *     out   = sum_j softmax(s)_j * v_j
+ *     lse   = ln sum_j exp(s_j)               (natural log)
+ * All arithmetic after the 16-bit loads is fp32.
+ *
+ * Conventions shared by all entry points:
+ *  - Pointers are DEVICE pointers unless marked (host).
+ *  - Every call enqueues its work on `stream` (a hipStream_t passed as
+ *    void *; NULL is the default stream) of the calling thread's current
+ *    device and returns without synchronising. Nothing is allocated or
+ *    freed; no pointer is kept after the call returns.
+ *  - The caller owns every buffer. Host-checkable argument errors return a
+ *    non-zero status BEFORE anything is launched, so no partial work happens.
+ *  - Device metadata cannot be validated on the host without a sync. A
+ *    sequence with seq_lens[b] < T or > capacity, or whose block-table entries
+ *    needed for its tokens lie outside [0, num_blocks), gets NaN in every
+ *    output row (and its append writes nothing); no memory outside the
+ *    buffers described here is read or written for it.
+ *  - Tensor element types are kvc_dtype; K/V caches and q are f16 or bf16.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID = -1,     /* bad argument (null pointer, shape, range, alignment) */
+  KVC_ERR_UNSUPPORTED = -2, /* valid but not implemented (head size, dtype) */
+  KVC_ERR_WORKSPACE = -3,   /* workspace missing or smaller than kvc_workspace_bytes() */
+  KVC_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+} kvc_status;
+
+typedef enum { KVC_F16 = 0, KVC_BF16 = 1, KVC_F32 = 2 } kvc_dtype;
+
+/*
+ * One layer's key cache and value cache (same layout, same dtype).
+ *
+ * Contiguous (block_table == NULL): element (b, head, token, h) of the key
+ * cache is k[b * stride_seq + head * stride_head + token * stride_tok + h];
+ * the default layout [B, K, capacity, H] has stride_seq = K * capacity * H,
+ * stride_head = capacity * H, stride_tok = H. A whole-model tensor
+ * [L, 2, K, C, H] is described per layer by pointer offsets with the same
+ * strides.
+ *
+ * Paged (block_table != NULL): k and v are pools of num_blocks blocks;
+ * logical token t of sequence b is stored in physical block
+ * p = block_table[b * max_blocks_per_seq + t / block_size] at slot
+ * t % block_size, i.e. element (p, head, slot, h) is
+ * k[p * stride_seq + head * stride_head + slot * stride_tok + h]; the default
+ * pool layout [num_blocks, K, block_size, H] has stride_seq =
+ * K * block_size * H, stride_head = block_size * H, stride_tok = H.
+ * Entries that no valid token needs are never read (use -1). Several
+ * sequences may map to the same physical block (shared prefixes); appends
+ * must not target a shared block.
+ *
+ * Strides are in elements; the head dimension is unit-stride. k, v and every
+ * stride times the element size must be multiples of 16 bytes.
+ */
+typedef struct kvc_cache {
+  void *k;                    /* device */
+  void *v;                    /* device */
+  const int32_t *block_table; /* device [B, max_blocks_per_seq] or NULL */
+  int64_t stride_seq;         /* elements between sequences (contiguous) or blocks (paged) */
+  int64_t stride_head;        /* elements between key-value heads */
+  int64_t stride_tok;         /* elements between tokens (slots) */
+  int32_t dtype;              /* kvc_dtype: KVC_F16 or KVC_BF16 */
+  int32_t capacity;           /* contiguous: max tokens per sequence; paged: ignored
+                                 (capacity is max_blocks_per_seq * block_size) */
+  int32_t block_size;         /* paged: tokens per block, a power of two, 1 .. 4096 */
+  int32_t max_blocks_per_seq; /* paged: row length of block_table */
+  int32_t num_blocks;         /* paged: blocks in each pool */
+  int32_t reserved;           /* must be 0 */
+} kvc_cache;
+
+/*
+ * Append the T new key and value rows of every sequence to its cache.
+ * Prior art: the kernel that writes the next target tokens to their
+ * positions in "Accelerating Sonar through speculation", section
+ * "Single-token MTP schedule".
+ *
+ * k_new, v_new: [B, T, K, H] contiguous, in cache->dtype. Row t of sequence b
+ * is written at logical position seq_lens[b] - T + t. Bytes are copied
+ * unchanged (bit-exact). Nothing else in the cache is written.
+ * Errors: KVC_ERR_INVALID for null pointers, B < 0, T < 1, K < 1, bad
+ * strides or alignment; KVC_ERR_UNSUPPORTED for H not in {64, 128} or a
+ * dtype other than f16/bf16. B == 0 succeeds and launches nothing.
+ */
+kvc_status kvc_append(const kvc_cache *cache, const void *k_new, const void *v_new, int B, int T,
+                      int K, int H, const int32_t *seq_lens, void *stream);
+
+/*
+ * Decode: one new query token per sequence (T = 1). Same as
+ * kvc_attn_verify with T = 1.
+ *
+ * q: [B, N, H] in cache->dtype. out: [B, N, H] in out_dtype (f32, f16 or
+ * bf16; 16-bit outputs are rounded to nearest even). lse: [B, N] fp32, or
+ * NULL. max_seq_len (host) is an upper bound on seq_lens[] used only to size
+ * the launch (a longer device length is still computed correctly, just with
+ * fewer workgroups than ideal); it must satisfy 1 <= max_seq_len <= capacity.
+ * scale multiplies q.k (1/sqrt(H) is the usual choice).
+ * num_workgroups: how many workgroups share the work (0 = automatic); the
+ * result is the same function for every value, up to fp32 rounding order.
+ * workspace: device scratch of at least kvc_workspace_bytes(B, 1, N, K, H,
+ * max_seq_len, num_workgroups) bytes, ZERO-FILLED when first allocated; every
+ * call leaves it zero-filled again, so it may be reused by later calls on
+ * the same stream. Calls that overlap in time must not share a workspace.
+ * Errors: as kvc_append, plus KVC_ERR_INVALID for N < 1, N % K != 0,
+ * max_seq_len out of range; KVC_ERR_WORKSPACE for a missing or small
+ * workspace.
+ */
+kvc_status kvc_attn_decode(const kvc_cache *cache, const void *q, void *out, int out_dtype,
+                           float *lse, int B, int N, int K, int H, const int32_t *seq_lens,
+                           int max_seq_len, float scale, int num_workgroups, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * Verify: T new query tokens per sequence (1 <= T <= 16), causal inside the
+ * block: token t sees the P_b prior keys and new tokens 0 .. t.
+ * q: [B, T, N, H]; out: [B, T, N, H]; lse: [B, T, N] fp32 or NULL.
+ * Other arguments and errors as kvc_attn_decode (max_seq_len >= T).
+ */
+kvc_status kvc_attn_verify(const kvc_cache *cache, const void *q, void *out, int out_dtype,
+                           float *lse, int B, int T, int N, int K, int H, const int32_t *seq_lens,
+                           int max_seq_len, float scale, int num_workgroups, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * Host query: workspace bytes needed by kvc_attn_decode (T = 1) or
+ * kvc_attn_verify with the same B, T, N, K, H, max_seq_len and
+ * num_workgroups. Returns 0 for invalid shapes. Uses the current device's
+ * compute-unit count when a device is present.
+ */
+size_t kvc_workspace_bytes(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups);
+
+/* Host: a static, human-readable name for a status code. */
+const char *kvc_status_string(kvc_status status);
+
+/*
+ * Test export: copy the first seq_lens[b] logical tokens of every sequence
+ * of a PAGED cache into contiguous dst_k, dst_v [B, K, max_seq_len, H]
+ * (cache->dtype), bit-exact. Rows at or beyond seq_lens[b] are not written.
+ * A sequence with seq_lens[b] > max_seq_len, or a needed block-table entry
+ * outside [0, num_blocks), is skipped. Errors as kvc_append.
+ */
+kvc_status kvc_gather(const kvc_cache *paged, void *dst_k, void *dst_v, int B, int K, int H,
+                      const int32_t *seq_lens, int max_seq_len, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,88 @@
+"""ctypes view of ``libkvc.so`` (declared in ``include/kvc.h``).
+
+Loading fails loudly when the library has not been built; there is no other
+implementation behind these names.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvc.so")
+
+KVC_OK = 0
+KVC_ERR_INVALID = -1
+KVC_ERR_UNSUPPORTED = -2
+KVC_ERR_WORKSPACE = -3
+KVC_ERR_HIP = -4
+
+KVC_F16 = 0
+KVC_BF16 = 1
+KVC_F32 = 2
+
+# Every symbol the header declares, in declaration order.
+EXPORTS = (
+    "kvc_append",
+    "kvc_attn_decode",
+    "kvc_attn_verify",
+    "kvc_workspace_bytes",
+    "kvc_status_string",
+    "kvc_gather",
+)
+
+
+class KvcCache(ctypes.Structure):
+    """Mirror of ``struct kvc_cache``."""
+
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("stride_seq", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+        ("stride_tok", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and return the library with its signatures set."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -m kv_cached_gqa_attention_amd.build` "
+            "(or __graft_entry__.build())"
+        )
+    lib = ctypes.CDLL(p)
+    c_int, c_float, c_size_t, vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    cache_p = ctypes.POINTER(KvcCache)
+    lib.kvc_append.argtypes = [cache_p, vp, vp, c_int, c_int, c_int, c_int, vp, vp]
+    lib.kvc_append.restype = c_int
+    lib.kvc_attn_decode.argtypes = [cache_p, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, vp,
+                                    c_int, c_float, c_int, vp, c_size_t, vp]
+    lib.kvc_attn_decode.restype = c_int
+    lib.kvc_attn_verify.argtypes = [cache_p, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
+                                    vp, c_int, c_float, c_int, vp, c_size_t, vp]
+    lib.kvc_attn_verify.restype = c_int
+    lib.kvc_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int]
+    lib.kvc_workspace_bytes.restype = c_size_t
+    lib.kvc_status_string.argtypes = [c_int]
+    lib.kvc_status_string.restype = ctypes.c_char_p
+    lib.kvc_gather.argtypes = [cache_p, vp, vp, c_int, c_int, c_int, vp, c_int, vp]
+    lib.kvc_gather.restype = c_int
+    if path is None:
+        _lib = lib
+    return lib

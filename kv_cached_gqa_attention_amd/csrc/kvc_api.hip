@@ -1,0 +1,280 @@
+// C entry points: argument checks, launch plan, dispatch.
+//
+// The plan never reads device data: sequence lengths and block tables stay on
+// the device and the kernels divide the work among themselves from them
+// ("Accelerating Sonar through speculation", section "Inference with
+// speculative decoding": metadata is copied to GPU memory before the model
+// runs, and syncing the GPU to the CPU on sequence lengths is the cost to
+// avoid). The host only fixes the grid size and the workspace layout.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kvc.h"
+#include "kvc_internal.h"
+
+namespace {
+
+using kvc::AttnArgs;
+using kvc::CopyArgs;
+
+constexpr int MAX_B = 4096;            // sequences per call (per-workgroup LDS prefix table)
+constexpr int VALU_MAX_ROWS = 8;       // G * T up to this uses the vector-ALU kernel
+constexpr int MFMA_MAX_NB = 4;         // 16-row blocks per matrix-core unit
+constexpr int MIN_TILES_PER_WG = 4;    // do not spread fewer tiles over a workgroup
+constexpr int VALU_WG_PER_CU = 4;
+constexpr int MFMA_WG_PER_CU = 2;
+constexpr int DEFAULT_CUS = 256;
+
+int device_cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return DEFAULT_CUS;
+  }
+  if (cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = DEFAULT_CUS;
+  }
+  cached[dev] = n;
+  return n;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  bool mfma;
+  int R, RB, RMAX, units, W;
+  size_t off_ml, off_cnt, bytes;
+};
+
+bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, Plan* p) {
+  if (B < 1 || T < 1 || T > 16 || N < 1 || K < 1 || N % K || (H != 64 && H != 128) ||
+      max_seq_len < 1 || num_wg < 0 || B > MAX_B)
+    return false;
+  const int G = N / K;
+  p->R = G * T;
+  if (p->R <= VALU_MAX_ROWS) {
+    p->mfma = false;
+    p->RB = 1;
+    p->RMAX = p->R;
+  } else {
+    p->mfma = true;
+    const int nb_total = (p->R + 15) / 16;
+    p->RB = (nb_total + MFMA_MAX_NB - 1) / MFMA_MAX_NB;
+    const int nb = (nb_total + p->RB - 1) / p->RB;
+    p->RMAX = nb * 16;
+  }
+  const int64_t units = (int64_t)B * K * p->RB;
+  if (units > (1 << 24)) return false;
+  p->units = (int)units;
+  if (num_wg > 0) {
+    p->W = num_wg > (1 << 20) ? (1 << 20) : num_wg;
+  } else {
+    const int64_t tiles_ub = units * ((max_seq_len + kvc::TILE - 1) / kvc::TILE);
+    const int64_t full = (int64_t)device_cu_count() * (p->mfma ? MFMA_WG_PER_CU : VALU_WG_PER_CU);
+    int64_t want = (tiles_ub + MIN_TILES_PER_WG - 1) / MIN_TILES_PER_WG;
+    if (want > full) want = full;
+    p->W = (int)(want < 1 ? 1 : want);
+  }
+  const size_t slots = (size_t)p->W + (size_t)p->units;
+  p->off_ml = align_up(slots * p->RMAX * H * sizeof(float), 256);
+  p->off_cnt = p->off_ml + align_up(slots * p->RMAX * 2 * sizeof(float), 256);
+  p->bytes = p->off_cnt + align_up((size_t)p->units * sizeof(int32_t), 256);
+  return true;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int log2_exact(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return ((1 << s) == v) ? s : -1;
+}
+
+// Shared cache checks; fills capacity (tokens) and block shift.
+kvc_status check_cache(const kvc_cache* c, int K, int H, int* capacity, int* shift) {
+  if (!c || !c->k || !c->v || c->reserved != 0) return KVC_ERR_INVALID;
+  if (c->dtype != KVC_F16 && c->dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+  if (H != 64 && H != 128) return KVC_ERR_UNSUPPORTED;
+  if (K < 1) return KVC_ERR_INVALID;
+  if (!aligned16(c->k) || !aligned16(c->v)) return KVC_ERR_INVALID;
+  if (c->stride_seq < 0 || c->stride_head < 0 || c->stride_tok < 0) return KVC_ERR_INVALID;
+  if ((c->stride_seq % 8) || (c->stride_head % 8) || (c->stride_tok % 8)) return KVC_ERR_INVALID;
+  if (c->block_table) {
+    const int s = log2_exact(c->block_size);
+    if (c->block_size < 1 || c->block_size > 4096 || s < 0) return KVC_ERR_INVALID;
+    if (c->max_blocks_per_seq < 1 || c->num_blocks < 1) return KVC_ERR_INVALID;
+    const int64_t cap = (int64_t)c->max_blocks_per_seq * c->block_size;
+    *capacity = cap > INT32_MAX ? INT32_MAX : (int)cap;
+    *shift = s;
+  } else {
+    if (c->capacity < 1) return KVC_ERR_INVALID;
+    *capacity = c->capacity;
+    *shift = 0;
+  }
+  return KVC_OK;
+}
+
+kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dtype, float* lse,
+                       int B, int T, int N, int K, int H, const int32_t* seq_lens, int max_seq_len,
+                       float scale, int num_wg, void* ws, size_t ws_bytes, void* stream) {
+  int capacity = 0, shift = 0;
+  const kvc_status st = check_cache(c, K, H, &capacity, &shift);
+  if (st != KVC_OK) return st;
+  if (!q || !out || !seq_lens) return KVC_ERR_INVALID;
+  if (B < 0 || T < 1 || T > 16 || N < 1 || N % K || num_wg < 0) return KVC_ERR_INVALID;
+  if (out_dtype != KVC_F16 && out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (max_seq_len < T || max_seq_len > capacity) return KVC_ERR_INVALID;
+  if (!isfinite(scale)) return KVC_ERR_INVALID;
+  if (!aligned16(q)) return KVC_ERR_INVALID;
+  if (B > MAX_B) return KVC_ERR_UNSUPPORTED;
+  if (B == 0) return KVC_OK;
+  Plan p;
+  if (!make_plan(B, T, N, K, H, max_seq_len, num_wg, &p)) return KVC_ERR_INVALID;
+  if (!ws || ws_bytes < p.bytes || !aligned16(ws)) return KVC_ERR_WORKSPACE;
+
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = static_cast<const char*>(c->k);
+  a.v = static_cast<const char*>(c->v);
+  a.table = c->block_table;
+  a.stride_seq = c->stride_seq * 2;
+  a.stride_head = c->stride_head * 2;
+  a.stride_tok = c->stride_tok * 2;
+  a.capacity = capacity;
+  a.block_shift = shift;
+  a.max_blocks = c->block_table ? c->max_blocks_per_seq : 0;
+  a.num_blocks = c->block_table ? c->num_blocks : 0;
+  a.q = static_cast<const char*>(q);
+  a.out = out;
+  a.lse = lse;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.T = T;
+  a.N = N;
+  a.K = K;
+  a.G = N / K;
+  a.R = p.R;
+  a.RB = p.RB;
+  a.RMAX = p.RMAX;
+  a.out_dtype = out_dtype;
+  a.W = p.W;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  char* w = static_cast<char*>(ws);
+  a.part_o = reinterpret_cast<float*>(w);
+  a.part_ml = reinterpret_cast<float*>(w + p.off_ml);
+  a.counters = reinterpret_cast<int32_t*>(w + p.off_cnt);
+
+  const bool bf = c->dtype == KVC_BF16;
+  const bool paged = c->block_table != nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = p.mfma ? kvc::launch_attn_mfma(a, bf, H, paged, s)
+                              : kvc::launch_attn_valu(a, bf, H, paged, s);
+  return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_append(const kvc_cache* cache, const void* k_new, const void* v_new, int B, int T,
+                      int K, int H, const int32_t* seq_lens, void* stream) {
+  int capacity = 0, shift = 0;
+  const kvc_status st = check_cache(cache, K, H, &capacity, &shift);
+  if (st != KVC_OK) return st;
+  if (!k_new || !v_new || !seq_lens || B < 0 || T < 1) return KVC_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVC_ERR_INVALID;
+  if (B == 0) return KVC_OK;
+  CopyArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = static_cast<char*>(cache->k);
+  a.v = static_cast<char*>(cache->v);
+  a.table = cache->block_table;
+  a.stride_seq = cache->stride_seq * 2;
+  a.stride_head = cache->stride_head * 2;
+  a.stride_tok = cache->stride_tok * 2;
+  a.capacity = capacity;
+  a.block_shift = shift;
+  a.max_blocks = cache->block_table ? cache->max_blocks_per_seq : 0;
+  a.num_blocks = cache->block_table ? cache->num_blocks : 0;
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.T = T;
+  a.K = K;
+  a.H = H;
+  const hipError_t e = kvc::launch_append(a, cache->block_table != nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+kvc_status kvc_attn_decode(const kvc_cache* cache, const void* q, void* out, int out_dtype,
+                           float* lse, int B, int N, int K, int H, const int32_t* seq_lens,
+                           int max_seq_len, float scale, int num_workgroups, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return attn_common(cache, q, out, out_dtype, lse, B, 1, N, K, H, seq_lens, max_seq_len, scale,
+                     num_workgroups, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_attn_verify(const kvc_cache* cache, const void* q, void* out, int out_dtype,
+                           float* lse, int B, int T, int N, int K, int H, const int32_t* seq_lens,
+                           int max_seq_len, float scale, int num_workgroups, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return attn_common(cache, q, out, out_dtype, lse, B, T, N, K, H, seq_lens, max_seq_len, scale,
+                     num_workgroups, workspace, workspace_bytes, stream);
+}
+
+size_t kvc_workspace_bytes(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups) {
+  Plan p;
+  if (!make_plan(B, T, N, K, H, max_seq_len, num_workgroups, &p)) return 0;
+  return p.bytes;
+}
+
+const char* kvc_status_string(kvc_status status) {
+  switch (status) {
+    case KVC_OK: return "KVC_OK";
+    case KVC_ERR_INVALID: return "KVC_ERR_INVALID: invalid argument";
+    case KVC_ERR_UNSUPPORTED: return "KVC_ERR_UNSUPPORTED: unsupported head size, dtype or batch";
+    case KVC_ERR_WORKSPACE: return "KVC_ERR_WORKSPACE: workspace missing or too small";
+    case KVC_ERR_HIP: return "KVC_ERR_HIP: HIP runtime error at launch";
+    default: return "unknown kvc_status";
+  }
+}
+
+kvc_status kvc_gather(const kvc_cache* paged, void* dst_k, void* dst_v, int B, int K, int H,
+                      const int32_t* seq_lens, int max_seq_len, void* stream) {
+  int capacity = 0, shift = 0;
+  const kvc_status st = check_cache(paged, K, H, &capacity, &shift);
+  if (st != KVC_OK) return st;
+  if (!paged->block_table || !dst_k || !dst_v || !seq_lens || B < 0 || max_seq_len < 1)
+    return KVC_ERR_INVALID;
+  if (!aligned16(dst_k) || !aligned16(dst_v)) return KVC_ERR_INVALID;
+  if (B == 0) return KVC_OK;
+  CopyArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = static_cast<char*>(paged->k);
+  a.v = static_cast<char*>(paged->v);
+  a.table = paged->block_table;
+  a.stride_seq = paged->stride_seq * 2;
+  a.stride_head = paged->stride_head * 2;
+  a.stride_tok = paged->stride_tok * 2;
+  a.capacity = capacity;
+  a.block_shift = shift;
+  a.max_blocks = paged->max_blocks_per_seq;
+  a.num_blocks = paged->num_blocks;
+  a.dst_k = static_cast<char*>(dst_k);
+  a.dst_v = static_cast<char*>(dst_v);
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.K = K;
+  a.H = H;
+  a.max_seq_len = max_seq_len;
+  const hipError_t e = kvc::launch_gather(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,339 @@
+// Split-KV attention on the matrix cores, for units whose G * T query rows
+// make q.k and p.v real dense contractions (the speculative verify pass:
+// "Accelerating Sonar through speculation", section "Speculative decoding",
+// scores n drafted tokens in one target pass; with T = n + 1 tokens and G
+// query heads per key-value head, each K/V row serves G * T query rows).
+//
+// Per 32-token tile and wave (v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulate):
+//   S^T [32 tok x 16 q] = K [32 tok x H] . Q^T [H x 16 q]      per 16 query rows
+//   O^T [H x 16 q]     += V^T [H x 32 tok] . P^T [32 tok x 16 q]
+// Computing the transposed score block puts a query row in a lane column, so
+// its running max needs only two cross-lane steps, and P^T leaves the
+// accumulators already in the B-operand layout of the p.v product (the
+// token-to-k-slot map is chosen to make that true). V^T needs each lane to
+// hold 8 tokens of one h: eight lanes load 8 token rows and swap 16-bit
+// elements with an 8 x 8 register transpose (swizzle + DPP).
+// p is split into a 16-bit high part and a 16-bit remainder, each multiplied
+// by V on the matrix cores, so p.v keeps close to fp32 precision.
+#include "kvc_device.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+typedef __attribute__((ext_vector_type(4))) float floatx4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+
+template <bool BF>
+__device__ __forceinline__ floatx4 mfma16(uint4 a, uint4 b, floatx4 c) {
+  if constexpr (BF) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+template <bool BF>
+__device__ __forceinline__ uint32_t to16(float f) {
+  if constexpr (BF) return f32_to_bf16_bits(f);
+  else return f32_to_f16_bits(f);
+}
+template <bool BF>
+__device__ __forceinline__ float from16(uint32_t bits) {
+  if constexpr (BF) return __uint_as_float(bits << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ uint32_t swz_xor4(uint32_t x) {
+  // ds_swizzle bit-mask mode: and 0x1f, or 0, xor 4 (within 32-lane halves)
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x101F);
+}
+
+// 8 x 8 transpose of 16-bit elements across the 8 lanes of an aligned lane
+// octet: lane i holds x_i[0..7] (element 2w in the low half of word w), and
+// receives y_i[j] = x_j[i]. Block swaps of 4, 2, then 1 element(s).
+__device__ __forceinline__ uint4 transpose8(uint4 v, int i8) {
+  uint32_t x0 = v.x, x1 = v.y, x2 = v.z, x3 = v.w;
+  const bool b2 = (i8 & 4) != 0, b1 = (i8 & 2) != 0, b0 = (i8 & 1) != 0;
+  uint32_t s0 = b2 ? x0 : x2, s1 = b2 ? x1 : x3;
+  uint32_t r0 = swz_xor4(s0), r1 = swz_xor4(s1);
+  if (b2) { x0 = r0; x1 = r1; } else { x2 = r0; x3 = r1; }
+  s0 = b1 ? x0 : x1;
+  s1 = b1 ? x2 : x3;
+  r0 = dpp_u<DPP_QUAD_XOR2>(s0);
+  r1 = dpp_u<DPP_QUAD_XOR2>(s1);
+  if (b1) { x0 = r0; x2 = r1; } else { x1 = r0; x3 = r1; }
+  uint32_t p0 = dpp_u<DPP_QUAD_XOR1>(x0), p1 = dpp_u<DPP_QUAD_XOR1>(x1);
+  uint32_t p2 = dpp_u<DPP_QUAD_XOR1>(x2), p3 = dpp_u<DPP_QUAD_XOR1>(x3);
+  if (b0) {
+    x0 = (x0 & 0xffff0000u) | (p0 >> 16);
+    x1 = (x1 & 0xffff0000u) | (p1 >> 16);
+    x2 = (x2 & 0xffff0000u) | (p2 >> 16);
+    x3 = (x3 & 0xffff0000u) | (p3 >> 16);
+  } else {
+    x0 = (x0 & 0xffffu) | (p0 << 16);
+    x1 = (x1 & 0xffffu) | (p1 << 16);
+    x2 = (x2 & 0xffffu) | (p2 << 16);
+    x3 = (x3 & 0xffffu) | (p3 << 16);
+  }
+  return make_uint4(x0, x1, x2, x3);
+}
+
+template <bool BF, int H, int NB, bool PAGED>
+__global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int RMAX = NB * 16;  // query rows per unit (row block)
+  constexpr int KS = H / 32;     // k-steps of S^T over h
+  constexpr int MH = H / 16;     // 16-row h blocks of O^T
+
+  extern __shared__ int32_t s_pre[];  // [B + 1]
+  __shared__ float s_m[RMAX], s_l[RMAX];
+  __shared__ float s_o[RMAX * H];
+  __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[1];
+
+  build_tile_prefix(a, s_pre, s_wave);
+  fill_invalid<H>(a);
+  const Partition part = make_partition(a, s_pre);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15;   // column (query row) / A-row (token or h) within a 16 block
+  const int g = lane >> 4;   // k-slot group
+  const int i8 = lane & 7;   // lane within its transpose octet
+  const int hb = c >> 3;     // which 8 of the 16 h of a block this octet loads
+  // token of k-slot (g, j): j < 4 -> 4g + j ; j >= 4 -> 16 + 4g + (j - 4)
+  const int vtok = (i8 < 4) ? (4 * g + i8) : (16 + 4 * g + i8 - 4);
+
+  for (int64_t x = part.lo; x < part.hi;) {
+    const Segment s = find_segment(a, s_pre, part, x);
+    x += s.t_end - s.t_begin;
+
+    // Q^T fragments (B operand): query row rb*RMAX + 16 nb + c, h = 32 ks + 8 g + j.
+    uint4 qf[NB][KS];
+    int vis[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int rr = s.rb * RMAX + nb * 16 + c;
+      if (rr < a.R) {
+        const char* qrow = a.q + row_index(a, s.b, s.k, rr) * (H * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = load16(qrow + (ks * 32 + g * 8) * 2);
+        vis[nb] = s.seq_len - a.T + rr / a.G + 1;
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = make_uint4(0, 0, 0, 0);
+        vis[nb] = s.seq_len;
+      }
+    }
+
+    const char* kb = a.k + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
+    const char* vb = a.v + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
+    const int32_t* trow = PAGED ? a.table + (int64_t)s.b * a.max_blocks : nullptr;
+    const int bmask = (1 << a.block_shift) - 1;
+    bool bad = false;
+    auto row_off = [&](int tok) -> int64_t {
+      tok = min(tok, s.seq_len - 1);
+      if constexpr (PAGED) {
+        int blk = trow[tok >> a.block_shift];
+        if ((unsigned)blk >= (unsigned)a.num_blocks) {
+          bad = true;
+          blk = 0;
+        }
+        return (int64_t)blk * a.stride_seq + (int64_t)(tok & bmask) * a.stride_tok;
+      } else {
+        return (int64_t)tok * a.stride_tok;
+      }
+    };
+
+    floatx4 ot[MH][NB];
+#pragma unroll
+    for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) ot[mh][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m[NB], l[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m[nb] = NEG_BIG;
+      l[nb] = 0.f;
+    }
+
+    uint4 kf[2][KS], vf[MH];
+    int ti = s.t_begin + wave;
+    if (ti < s.t_end) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int64_t off = row_off(ti * TILE + mb * 16 + c);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[mb][ks] = load16(kb + off + (ks * 32 + g * 8) * 2);
+      }
+      const int64_t offv = row_off(ti * TILE + vtok);
+#pragma unroll
+      for (int mh = 0; mh < MH; ++mh) vf[mh] = load16(vb + offv + (mh * 16 + hb * 8) * 2);
+    }
+
+    for (; ti < s.t_end; ti += WAVES) {
+      // ---- S^T = K . Q^T
+      floatx4 st[2][NB];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16<BF>(kf[mb][ks], qf[nb][ks], acc);
+          st[mb][nb] = acc;
+        }
+
+      // ---- next tile's K
+      const int tn = ti + WAVES;
+      if (tn < s.t_end) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int64_t off = row_off(tn * TILE + mb * 16 + c);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kf[mb][ks] = load16(kb + off + (ks * 32 + g * 8) * 2);
+        }
+      }
+
+      // ---- scale, mask, online softmax (one query row per lane column)
+      const int tok0 = ti * TILE;
+      const bool edge = tok0 + TILE > s.seq_len - a.T + 1;
+      uint4 phi[NB], plo[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float p[2][4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = st[mb][nb][i] * a.scale_log2;
+            if (edge && tok0 + mb * 16 + 4 * g + i >= vis[nb]) v = -__builtin_inff();
+            p[mb][i] = v;
+          }
+        float mt = p[0][0];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, p[mb][i]);
+        mt = fmaxf(mt, shfl_xor_f(mt, 16));
+        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        const float mn = fmaxf(m[nb], mt);
+        if (mn > m[nb]) {
+          const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);
+          l[nb] *= alpha;
+#pragma unroll
+          for (int mh = 0; mh < MH; ++mh) ot[mh][nb] *= alpha;
+          m[nb] = mn;
+        }
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float e0 = __builtin_amdgcn_exp2f(p[mb][i] - m[nb]);
+            const float e1 = __builtin_amdgcn_exp2f(p[mb][i + 1] - m[nb]);
+            l[nb] += e0 + e1;
+            const uint32_t h0 = to16<BF>(e0), h1 = to16<BF>(e1);
+            const uint32_t l0 = to16<BF>(e0 - from16<BF>(h0)), l1 = to16<BF>(e1 - from16<BF>(h1));
+            hw[mb * 2 + i / 2] = h0 | (h1 << 16);
+            lw[mb * 2 + i / 2] = l0 | (l1 << 16);
+          }
+        phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
+
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int mh = 0; mh < MH; ++mh) {
+        const uint4 vt = transpose8(vf[mh], i8);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          ot[mh][nb] = mfma16<BF>(vt, phi[nb], ot[mh][nb]);
+          ot[mh][nb] = mfma16<BF>(vt, plo[nb], ot[mh][nb]);
+        }
+      }
+
+      // ---- next tile's V
+      if (tn < s.t_end) {
+        const int64_t offv = row_off(tn * TILE + vtok);
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh) vf[mh] = load16(vb + offv + (mh * 16 + hb * 8) * 2);
+      }
+    }
+
+    // ---- per-column totals of l (lanes of one column hold different tokens)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      l[nb] += shfl_xor_f(l[nb], 16);
+      l[nb] += shfl_xor_f(l[nb], 32);
+    }
+    {
+      const unsigned long long anybad = __ballot(bad);
+      if (lane == 0) s_bad[wave] = anybad != 0ull;
+    }
+    // ---- fold the four waves into one state in LDS, one wave at a time
+    for (int w = 0; w < WAVES; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = nb * 16 + c;
+          float sp = 0.f, sw = 1.f, M = m[nb];
+          if (w > 0) {
+            const float mp = s_m[col];
+            M = fmaxf(mp, m[nb]);
+            sp = __builtin_amdgcn_exp2f(mp - M);
+            sw = __builtin_amdgcn_exp2f(m[nb] - M);
+          }
+#pragma unroll
+          for (int mh = 0; mh < MH; ++mh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float* dst = &s_o[col * H + mh * 16 + 4 * g + i];
+              *dst = (w > 0 ? *dst * sp : 0.f) + ot[mh][nb][i] * sw;
+            }
+          if (g == 0) {
+            s_l[col] = (w > 0 ? s_l[col] * sp : 0.f) + l[nb] * sw;
+            s_m[col] = M;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    bool segbad = false;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
+    finish_segment<H, 1>(a, s, s_m, s_l, s_o, segbad, s_flag);
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <bool BF, int H, int NB, bool PAGED>
+static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
+  const size_t shmem = (size_t)(a.B + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL((attn_mfma_kernel<BF, H, NB, PAGED>), dim3(a.W), dim3(THREADS), shmem, stream, a);
+  return hipGetLastError();
+}
+
+template <bool BF, int H, bool PAGED>
+static hipError_t launch_mfma_nb(const AttnArgs& a, hipStream_t stream) {
+  switch (a.RMAX / 16) {
+    case 1: return launch_mfma_t<BF, H, 1, PAGED>(a, stream);
+    case 2: return launch_mfma_t<BF, H, 2, PAGED>(a, stream);
+    case 3: return launch_mfma_t<BF, H, 3, PAGED>(a, stream);
+    case 4: return launch_mfma_t<BF, H, 4, PAGED>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {
+  if (bf16) {
+    if (H == 64) return paged ? launch_mfma_nb<true, 64, true>(a, stream) : launch_mfma_nb<true, 64, false>(a, stream);
+    return paged ? launch_mfma_nb<true, 128, true>(a, stream) : launch_mfma_nb<true, 128, false>(a, stream);
+  }
+  if (H == 64) return paged ? launch_mfma_nb<false, 64, true>(a, stream) : launch_mfma_nb<false, 64, false>(a, stream);
+  return paged ? launch_mfma_nb<false, 128, true>(a, stream) : launch_mfma_nb<false, 128, false>(a, stream);
+}
+
+}  // namespace kvc

@@ -1,0 +1,385 @@
+// Device-side building blocks shared by the attention kernels.
+//
+// Work partition. The independent unit of attention is (sequence b, key-value
+// head k, query-row block rb): one unit streams the K and V rows of head k of
+// sequence b once and serves all G * T query rows that read them ("Stanford
+// CS336 Day 13 - Inference", "Attention layers": scores B x S x T x K x G
+// against values B x S x K x H). A unit's keys are cut into 32-token tiles.
+// All units' tiles are laid end to end in (b, k, rb, tile) order and every
+// workgroup takes an equal contiguous share of that flat range, computed on
+// the device from seq_lens (no host read of lengths: "Accelerating Sonar
+// through speculation", section "Inference with speculative decoding").
+// A workgroup whose share covers part of a unit writes an online-softmax
+// partial (m, l, o) for it; the last workgroup to finish the unit merges the
+// partials by log-sum-exp. This is the split-KV idea that "CS336, lectures 10
+// and 12", section "PagedAttention", names FlashDecoding; the merge algebra is
+// the plain one: with partition sums l_s at maxima m_s,
+//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  o = sum_s o_s 2^(m_s - M) / L.
+// Scores are kept in base 2 (q.k * scale * log2 e) so exp2 is one instruction;
+// the natural-log LSE is (M + log2 L) * ln 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int TILE = 32;        // tokens per work tile
+constexpr int WAVES = 4;        // waves per workgroup
+constexpr int THREADS = 64 * WAVES;
+constexpr float NEG_BIG = -1.0e30f;  // running max before any visible key; exp2(NEG_BIG - x) == 0
+constexpr float LN2 = 0.69314718055994531f;
+
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf162_t;
+
+// Everything a kernel needs, passed by value.
+struct AttnArgs {
+  const char* k;  // byte pointers to the K and V caches (or pools)
+  const char* v;
+  const int32_t* table;  // paged: [B, max_blocks]; nullptr when contiguous
+  int64_t stride_seq;    // BYTES between sequences / blocks
+  int64_t stride_head;   // BYTES between key-value heads
+  int64_t stride_tok;    // BYTES between tokens / slots
+  int32_t capacity;      // largest valid seq_len
+  int32_t block_shift;   // paged: log2(block_size)
+  int32_t max_blocks;    // paged: block table row length
+  int32_t num_blocks;    // paged: pool size in blocks
+  const char* q;         // [B, T, N, H] in the cache dtype
+  void* out;             // [B, T, N, H] in out_dtype
+  float* lse;            // [B, T, N] or nullptr
+  const int32_t* seq_lens;
+  int32_t B, T, N, K, G;
+  int32_t R;     // G * T query rows per (b, k)
+  int32_t RB;    // query-row blocks per (b, k)
+  int32_t RMAX;  // rows per row block (the last block may be partial)
+  int32_t out_dtype;  // 0 f16, 1 bf16, 2 f32
+  int32_t W;          // launched workgroups
+  float scale_log2;   // scale * log2(e)
+  float* part_o;      // [W + units, RMAX, H]
+  float* part_ml;     // [W + units, RMAX, 2]
+  int32_t* counters;  // [units]
+};
+
+// ---------------------------------------------------------------- dtypes
+
+template <bool BF>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (BF) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                           __builtin_bit_cast(bf162_t, b), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                  c, false);
+  }
+}
+
+// Low / high 16-bit element of a packed pair, widened to fp32 (exact).
+template <bool BF>
+__device__ __forceinline__ float lo_f(uint32_t x) {
+  if constexpr (BF) {
+    return __uint_as_float(x << 16);
+  } else {
+    return (float)__builtin_bit_cast(half2_t, x)[0];
+  }
+}
+template <bool BF>
+__device__ __forceinline__ float hi_f(uint32_t x) {
+  if constexpr (BF) {
+    return __uint_as_float(x & 0xffff0000u);
+  } else {
+    return (float)__builtin_bit_cast(half2_t, x)[1];
+  }
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ void store_out(void* out, int64_t idx, int out_dtype, float v) {
+  if (out_dtype == 2) {
+    static_cast<float*>(out)[idx] = v;
+  } else if (out_dtype == 1) {
+    static_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(v);
+  } else {
+    static_cast<uint16_t*>(out)[idx] = f32_to_f16_bits(v);
+  }
+}
+
+__device__ __forceinline__ uint4 load16(const char* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+// DPP controls (GFX9 encoding).
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+// Sum over aligned groups of LANES (4, 8 or 16) consecutive lanes; every lane
+// of the group receives the total.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f<DPP_QUAD_XOR1>(x);
+  x += dpp_f<DPP_QUAD_XOR2>(x);
+  if constexpr (LANES >= 8) x += dpp_f<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (LANES >= 16) x += dpp_f<DPP_ROW_MIRROR>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) {
+  return __shfl_xor(x, m, 64);
+}
+
+// ---------------------------------------------------------------- partition
+
+__device__ __forceinline__ bool seq_valid(int32_t len, int32_t T, int32_t capacity) {
+  return len >= T && len <= capacity;
+}
+
+// s_pre[0..B]: exclusive prefix sums of tiles per sequence (0 for invalid
+// lengths). Requires THREADS threads and a scratch of WAVES ints.
+__device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_wave) {
+  const int tid = threadIdx.x;
+  const int per = (a.B + THREADS - 1) / THREADS;
+  const int b0 = tid * per;
+  int32_t local = 0;
+  for (int i = 0; i < per; ++i) {
+    int b = b0 + i;
+    if (b < a.B) {
+      int32_t len = a.seq_lens[b];
+      local += seq_valid(len, a.T, a.capacity) ? (len + TILE - 1) / TILE : 0;
+    }
+  }
+  // inclusive scan of `local` over the workgroup
+  const int lane = tid & 63;
+  int32_t incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int32_t y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_wave[tid >> 6] = incl;
+  __syncthreads();
+  int32_t carry = 0;
+  for (int w = 0; w < (tid >> 6); ++w) carry += s_wave[w];
+  int32_t run = carry + incl - local;  // exclusive prefix of this thread's chunk
+  for (int i = 0; i < per; ++i) {
+    int b = b0 + i;
+    if (b < a.B) {
+      s_pre[b] = run;
+      int32_t len = a.seq_lens[b];
+      run += seq_valid(len, a.T, a.capacity) ? (len + TILE - 1) / TILE : 0;
+    }
+  }
+  if (tid == THREADS - 1) s_pre[a.B] = carry + incl;
+  __syncthreads();
+}
+
+// The workgroup's view of one unit segment.
+struct Segment {
+  int b;          // sequence
+  int k;          // key-value head
+  int rb;         // query-row block
+  int unit;       // (b * K + k) * RB + rb
+  int seq_len;    // valid tokens
+  int t_begin;    // first tile of this segment (within the unit)
+  int t_end;      // one past the last tile
+  int n_parts;    // workgroups sharing the unit (1: this one writes the output directly)
+  int first_wg;   // first workgroup sharing the unit
+};
+
+struct Partition {
+  int64_t total;  // tiles over all units
+  int w_eff;      // workgroups with work: min(W, total)
+  int64_t lo, hi; // this workgroup's flat tile range
+  int krb;        // K * RB
+
+  __device__ int owner(int64_t x) const {  // workgroup whose range holds tile x
+    return (int)(((x + 1) * (int64_t)w_eff - 1) / total);
+  }
+};
+
+__device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int32_t* s_pre) {
+  Partition p;
+  p.krb = a.K * a.RB;
+  p.total = (int64_t)s_pre[a.B] * p.krb;
+  p.w_eff = (int)(p.total < (int64_t)a.W ? p.total : (int64_t)a.W);
+  const int w = blockIdx.x;
+  if (w < p.w_eff) {
+    p.lo = (int64_t)w * p.total / p.w_eff;
+    p.hi = (int64_t)(w + 1) * p.total / p.w_eff;
+  } else {
+    p.lo = p.hi = 0;
+  }
+  return p;
+}
+
+// Segment containing flat tile x (x < p.total).
+__device__ __forceinline__ Segment find_segment(const AttnArgs& a, const int32_t* s_pre,
+                                                const Partition& p, int64_t x) {
+  // first b with s_pre[b + 1] * krb > x
+  int lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if ((int64_t)s_pre[mid + 1] * p.krb > x) hi = mid; else lo = mid + 1;
+  }
+  Segment s;
+  s.b = lo;
+  const int64_t base = (int64_t)s_pre[lo] * p.krb;
+  const int tb = s_pre[lo + 1] - s_pre[lo];
+  const int64_t off = x - base;
+  const int ur = (int)(off / tb);
+  s.k = ur / a.RB;
+  s.rb = ur - s.k * a.RB;
+  s.unit = (s.b * a.K + s.k) * a.RB + s.rb;
+  s.seq_len = a.seq_lens[s.b];
+  s.t_begin = (int)(off - (int64_t)ur * tb);
+  const int64_t room = p.hi - x;
+  s.t_end = (int64_t)(tb - s.t_begin) < room ? tb : s.t_begin + (int)room;
+  const int64_t ustart = x - s.t_begin;
+  s.first_wg = p.owner(ustart);
+  s.n_parts = p.owner(ustart + tb - 1) - s.first_wg + 1;
+  return s;
+}
+
+// ---------------------------------------------------------------- outputs
+
+__device__ __forceinline__ int64_t row_index(const AttnArgs& a, int b, int k, int r) {
+  // query row r of unit (b, k) is (t, g) with r = t * G + g
+  const int t = r / a.G;
+  const int g = r - t * a.G;
+  return ((int64_t)b * a.T + t) * a.N + (int64_t)k * a.G + g;
+}
+
+// Final write of one (row, h) element from base-2 stats.
+__device__ __forceinline__ void write_final(const AttnArgs& a, int b, int k, int r, int H, int h,
+                                            float o_sum, float m, float l) {
+  const int64_t ri = row_index(a, b, k, r);
+  store_out(a.out, ri * H + h, a.out_dtype, o_sum / l);
+  if (h == 0 && a.lse) a.lse[ri] = (m + __log2f(l)) * LN2;
+}
+
+// NaN outputs for the rows of sequences with an invalid length. Units are
+// dealt round-robin to all launched workgroups.
+template <int H>
+__device__ void fill_invalid(const AttnArgs& a) {
+  const float qnan = __int_as_float(0x7fc00000);
+  const int units = a.B * a.K;
+  for (int u = blockIdx.x; u < units; u += a.W) {
+    const int b = u / a.K;
+    if (seq_valid(a.seq_lens[b], a.T, a.capacity)) continue;
+    const int k = u - b * a.K;
+    for (int e = threadIdx.x; e < a.R * H; e += THREADS) {
+      const int r = e / H, h = e - (e / H) * H;
+      const int64_t ri = row_index(a, b, k, r);
+      store_out(a.out, ri * H + h, a.out_dtype, qnan);
+      if (h == 0 && a.lse) a.lse[ri] = qnan;
+    }
+  }
+}
+
+// Finish one unit segment whose per-wave states sit in LDS:
+//   s_m[w * RMAX + r], s_l[w * RMAX + r], s_o[(w * RMAX + r) * H + h]
+// for NW wave states. Combines the waves, then either writes the output (the
+// segment is the whole unit) or writes a partial and, if this workgroup is
+// the last of the unit, merges all of the unit's partials. `bad` marks a
+// segment that met an out-of-range block-table entry: its partial is NaN.
+// Ends with a barrier, so LDS may be reused afterwards.
+template <int H, int NW>
+__device__ void finish_segment(const AttnArgs& a, const Segment& s, const float* s_m,
+                               const float* s_l, const float* s_o, bool bad, int32_t* s_flag) {
+  const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
+  const int row0 = s.rb * a.RMAX;
+  const float qnan = __int_as_float(0x7fc00000);
+  if (s.n_parts == 1) {
+    for (int e = threadIdx.x; e < rows * H; e += THREADS) {
+      const int r = e / H, h = e - (e / H) * H;
+      float M = NEG_BIG;
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * a.RMAX + r]);
+      float L = 0.f, O = 0.f;
+      for (int w = 0; w < NW; ++w) {
+        const float sc = exp2f(s_m[w * a.RMAX + r] - M);
+        L += sc * s_l[w * a.RMAX + r];
+        O += sc * s_o[(w * a.RMAX + r) * H + h];
+      }
+      if (bad) O = L = M = qnan;
+      write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
+    }
+    __syncthreads();
+    return;
+  }
+  const int slot = blockIdx.x + s.unit;
+  float* po = a.part_o + (int64_t)slot * a.RMAX * H;
+  float* pml = a.part_ml + (int64_t)slot * a.RMAX * 2;
+  for (int e = threadIdx.x; e < rows * H; e += THREADS) {
+    const int r = e / H, h = e - (e / H) * H;
+    float M = NEG_BIG;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * a.RMAX + r]);
+    float L = 0.f, O = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      const float sc = exp2f(s_m[w * a.RMAX + r] - M);
+      L += sc * s_l[w * a.RMAX + r];
+      O += sc * s_o[(w * a.RMAX + r) * H + h];
+    }
+    if (bad) O = L = M = qnan;
+    po[r * H + h] = O;
+    if (h == 0) {
+      pml[r * 2 + 0] = M;
+      pml[r * 2 + 1] = L;
+    }
+  }
+  // Release the partial to other workgroups (other XCDs included), then count.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(&a.counters[s.unit], 1);
+    s_flag[0] = (prev == s.n_parts - 1);
+  }
+  __syncthreads();
+  if (s_flag[0]) {
+    __threadfence();  // acquire the other workgroups' partials
+    for (int e = threadIdx.x; e < rows * H; e += THREADS) {
+      const int r = e / H, h = e - (e / H) * H;
+      float M = NEG_BIG;
+      for (int i = 0; i < s.n_parts; ++i) {
+        const float* ml = a.part_ml + (int64_t)(s.first_wg + i + s.unit) * a.RMAX * 2;
+        M = fmaxf(M, ml[r * 2]);
+      }
+      float L = 0.f, O = 0.f;
+      for (int i = 0; i < s.n_parts; ++i) {
+        const int64_t sl = s.first_wg + i + s.unit;
+        const float* ml = a.part_ml + sl * a.RMAX * 2;
+        const float mi = ml[r * 2];
+        const float li = ml[r * 2 + 1];
+        const float oi = a.part_o[(sl * a.RMAX + r) * H + h];
+        const float sc = exp2f(mi - M);
+        L += sc * li;
+        O += sc * oi;
+      }
+      write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
+    }
+    if (threadIdx.x == 0) atomicExch(&a.counters[s.unit], 0);
+  }
+  __syncthreads();
+}
+
+}  // namespace kvc

@@ -1,0 +1,31 @@
+// Host-side declarations shared by the C entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc_device.h"
+
+namespace kvc {
+
+// Cache description with byte strides, as the copy kernels take it.
+struct CopyArgs {
+  char* k;
+  char* v;
+  const int32_t* table;
+  int64_t stride_seq, stride_head, stride_tok;  // bytes
+  int32_t capacity, block_shift, max_blocks, num_blocks;
+  const char* k_new;  // append: [B, T, K, H]
+  const char* v_new;
+  char* dst_k;        // gather: [B, K, max_seq_len, H]
+  char* dst_v;
+  const int32_t* seq_lens;
+  int32_t B, T, K, H, max_seq_len;
+};
+
+hipError_t launch_append(const CopyArgs& a, bool paged, hipStream_t stream);
+hipError_t launch_gather(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_attn_valu(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream);
+hipError_t launch_attn_mfma(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream);
+
+}  // namespace kvc

@@ -1,0 +1,146 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments on the host before launching anything.
+
+Pointers passed here are fake (aligned, never dereferenced): every checked
+error returns before any device work.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cached_gqa_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libkvc.so is not built; run __graft_entry__.build() first")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _header_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header():
+    # 3 pointers + 3 int64 + 6 int32, no padding
+    assert ctypes.sizeof(_lib.KvcCache) == 3 * 8 + 3 * 8 + 6 * 4
+    assert _lib.KvcCache.stride_seq.offset == 24
+    assert _lib.KvcCache.dtype.offset == 48
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        s = lib.kvc_status_string(code).decode()
+        assert s.startswith("KVC_")
+    assert "unknown" in lib.kvc_status_string(7).decode()
+
+
+def test_workspace_bytes(lib):
+    assert lib.kvc_workspace_bytes(64, 1, 32, 8, 128, 4097, 0) > 0
+    assert lib.kvc_workspace_bytes(64, 1, 32, 8, 96, 4097, 0) == 0  # H
+    assert lib.kvc_workspace_bytes(64, 1, 30, 8, 128, 4097, 0) == 0  # N % K
+    assert lib.kvc_workspace_bytes(64, 17, 32, 8, 128, 4097, 0) == 0  # T
+    assert lib.kvc_workspace_bytes(0, 1, 32, 8, 128, 4097, 0) == 0  # B
+    a = lib.kvc_workspace_bytes(8, 5, 64, 8, 128, 9000, 100)
+    b = lib.kvc_workspace_bytes(8, 5, 64, 8, 128, 9000, 1000)
+    assert 0 < a < b
+
+
+def _cache(**kw):
+    c = _lib.KvcCache()
+    c.k = FAKE
+    c.v = FAKE * 2
+    c.block_table = None
+    c.stride_seq = 8 * 4096 * 128
+    c.stride_head = 4096 * 128
+    c.stride_tok = 128
+    c.dtype = _lib.KVC_BF16
+    c.capacity = 4096
+    c.block_size = 0
+    c.max_blocks_per_seq = 0
+    c.num_blocks = 0
+    c.reserved = 0
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _decode(lib, cache, B=64, N=32, K=8, H=128, max_seq_len=4096, out_dtype=_lib.KVC_F32, q=FAKE,
+            ws=FAKE, ws_bytes=1 << 30, scale=0.088, nwg=0, seq_lens=FAKE):
+    cp = ctypes.byref(cache) if cache is not None else None
+    return lib.kvc_attn_decode(cp, q, FAKE, out_dtype, None, B, N, K, H, seq_lens, max_seq_len,
+                               scale, nwg, ws, ws_bytes, None)
+
+
+def test_decode_host_errors(lib):
+    E = _lib
+    assert _decode(lib, None) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(k=None)) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(reserved=1)) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(dtype=E.KVC_F32)) == E.KVC_ERR_UNSUPPORTED
+    assert _decode(lib, _cache(), H=96) == E.KVC_ERR_UNSUPPORTED
+    assert _decode(lib, _cache(), N=30) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), max_seq_len=4097) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), max_seq_len=0) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), out_dtype=9) == E.KVC_ERR_UNSUPPORTED
+    assert _decode(lib, _cache(), q=FAKE + 2) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), q=None) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), seq_lens=None) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(stride_tok=100)) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(k=FAKE + 8)) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), scale=float("nan")) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), nwg=-1) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), B=5000) == E.KVC_ERR_UNSUPPORTED
+    assert _decode(lib, _cache(), ws=None) == E.KVC_ERR_WORKSPACE
+    assert _decode(lib, _cache(), ws_bytes=16) == E.KVC_ERR_WORKSPACE
+    # B == 0 is a successful no-op (nothing launched)
+    assert _decode(lib, _cache(), B=0) == E.KVC_OK
+
+
+def test_paged_descriptor_errors(lib):
+    E = _lib
+    paged = dict(block_table=FAKE * 3, block_size=16, max_blocks_per_seq=8192, num_blocks=100,
+                 stride_seq=8 * 16 * 128, stride_head=16 * 128)
+    assert _decode(lib, _cache(**paged), B=0, max_seq_len=131072) == E.KVC_OK
+    assert _decode(lib, _cache(**{**paged, "block_size": 12}), B=0) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(**{**paged, "num_blocks": 0}), B=0) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(**paged), B=0, max_seq_len=131073) == E.KVC_ERR_INVALID
+
+
+def test_verify_and_append_host_errors(lib):
+    E = _lib
+    c = _cache()
+    v = lambda T, **kw: lib.kvc_attn_verify(ctypes.byref(c), FAKE, FAKE, E.KVC_F32, None, 8, T,
+                                            kw.get("N", 64), 8, 128, FAKE, kw.get("L", 4096), 0.1, 0,
+                                            FAKE, 1 << 30, None)
+    assert v(0) == E.KVC_ERR_INVALID
+    assert v(17) == E.KVC_ERR_INVALID
+    assert v(5, L=4) == E.KVC_ERR_INVALID  # max_seq_len < T
+    ap = lambda **kw: lib.kvc_append(ctypes.byref(kw.get("c", c)), kw.get("kn", FAKE), FAKE,
+                                     kw.get("B", 8), kw.get("T", 1), 8, kw.get("H", 128), FAKE, None)
+    assert ap(T=0) == E.KVC_ERR_INVALID
+    assert ap(B=-1) == E.KVC_ERR_INVALID
+    assert ap(kn=None) == E.KVC_ERR_INVALID
+    assert ap(kn=FAKE + 4) == E.KVC_ERR_INVALID
+    assert ap(H=80) == E.KVC_ERR_UNSUPPORTED
+    assert ap(B=0) == E.KVC_OK
+    g = lambda cc: lib.kvc_gather(ctypes.byref(cc), FAKE, FAKE, 0, 8, 128, FAKE, 16, None)
+    assert g(c) == E.KVC_ERR_INVALID  # gather needs a paged cache

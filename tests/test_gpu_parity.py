@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerance (from the fp32-accumulation requirement): max |delta| <= 2e-3 on
+fp32 outputs and on the LSE; 16-bit outputs within 1 ulp of the oracle
+rounded to nearest even; appends and gathers bit-exact. Every cache is
+NaN-poisoned outside the valid rows, so a read of a row that must not be read
+shows up as a non-finite output.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cached_gqa_attention_amd as kvc
+from gpu_cases import all_units, compare_units, oracle_unit, run_case, say, ulp_distance_16
+from workloads import draw_inputs, layout_contiguous, layout_paged, logical_kv, make_block_table
+
+pytestmark = pytest.mark.gpu
+
+BF, HF = torch.bfloat16, torch.float16
+
+
+# ----------------------------------------------------------------- append / gather
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("dtype,H,T", [(BF, 128, 1), (HF, 64, 5), (BF, 64, 3)])
+def test_append_bit_exact(gpu_device, layout, dtype, H, T):
+    B, K = 5, 3
+    prior = np.array([0, 1, 15, 16, 40])
+    inp = draw_inputs(B, T, 6, K, H, dtype, prior, seed=31, device=gpu_device)
+    seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(gpu_device)
+    if layout == "contiguous":
+        ck, cv = layout_contiguous(inp, capacity=64)
+        cache = kvc.Cache(ck, cv)
+    else:
+        table, nb = make_block_table(5, inp.seq_lens, 16, extra_blocks=2)
+        pk, pv = layout_paged(inp, table, nb, 16)
+        cache = kvc.Cache(pk, pv, torch.from_numpy(table).to(gpu_device))
+    before_k, before_v = cache.k.clone(), cache.v.clone()
+    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+    torch.cuda.synchronize()
+    exp_k, exp_v = before_k.clone(), before_v.clone()
+    for b in range(B):
+        for t in range(T):
+            pos = int(inp.seq_lens[b]) - T + t
+            if layout == "contiguous":
+                exp_k[b, :, pos, :] = inp.k_new[b, t]
+                exp_v[b, :, pos, :] = inp.v_new[b, t]
+            else:
+                blk = int(table[b, pos // 16])
+                exp_k[blk, :, pos % 16, :] = inp.k_new[b, t]
+                exp_v[blk, :, pos % 16, :] = inp.v_new[b, t]
+    as_int = lambda t: t.view(torch.int16)
+    assert torch.equal(as_int(cache.k), as_int(exp_k))  # bitwise, NaN padding included
+    assert torch.equal(as_int(cache.v), as_int(exp_v))
+
+
+def test_gather_bit_exact(gpu_device):
+    B, T, K, H = 4, 2, 2, 128
+    prior = np.array([0, 17, 33, 100])
+    inp = draw_inputs(B, T, 4, K, H, BF, prior, seed=32, device=gpu_device)
+    seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(gpu_device)
+    table, nb = make_block_table(9, inp.seq_lens, 16, extra_blocks=5)
+    pk, pv = layout_paged(inp, table, nb, 16)
+    cache = kvc.Cache(pk, pv, torch.from_numpy(table).to(gpu_device))
+    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+    L = int(inp.seq_lens.max())
+    dk, dv = kvc.gather(cache, seq_lens, L)
+    torch.cuda.synchronize()
+    for b in range(B):
+        kb, vb = logical_kv(inp, b)
+        n = int(inp.seq_lens[b])
+        assert torch.equal(dk[b, :, :n].permute(1, 0, 2).view(torch.int16), kb.view(torch.int16))
+        assert torch.equal(dv[b, :, :n].permute(1, 0, 2).view(torch.int16), vb.view(torch.int16))
+
+
+# ----------------------------------------------------------------- attention parity
+
+SMALL = [
+    # B, T, N, K, H, dtype, prior
+    (1, 1, 14, 2, 64, HF, [295]),                 # the measured model's shape (G = 7)
+    (3, 1, 8, 8, 128, BF, [0, 31, 200]),          # MHA (G = 1), empty prior context
+    (4, 1, 8, 4, 64, BF, [1, 32, 33, 97]),        # G = 2
+    (5, 1, 32, 8, 128, BF, [512, 700, 64, 1025, 3]),  # G = 4, the batched-decode shape
+    (2, 1, 16, 2, 128, HF, [63, 130]),            # G = 8
+    (2, 1, 6, 1, 64, HF, [40, 77]),               # MQA (K = 1, G = N = 6)
+    (2, 1, 32, 1, 128, BF, [90, 260]),            # MQA, G = 32 -> matrix cores
+    (2, 2, 8, 2, 128, BF, [10, 300]),             # verify, G*T = 8 (vector path)
+    (3, 3, 4, 2, 64, HF, [0, 5, 77]),             # verify, G*T = 6
+    (2, 5, 64, 8, 128, BF, [100, 555]),           # verify, G*T = 40 (the verify shape)
+    (2, 4, 16, 4, 64, HF, [33, 129]),             # verify, G*T = 16
+    (2, 8, 8, 1, 128, BF, [50, 1000]),            # verify, G*T = 64
+    (1, 16, 32, 4, 128, BF, [300]),               # verify, G*T = 128 -> two row blocks
+    (2, 7, 14, 2, 64, HF, [0, 66]),               # verify, G*T = 49, empty prior
+]
+
+
+def _ids(cases):
+    return [f"B{c[0]}T{c[1]}N{c[2]}K{c[3]}H{c[4]}{'bf' if c[5] is BF else 'hf'}" for c in cases]
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("case", SMALL, ids=_ids(SMALL))
+def test_attention_parity_fp32(gpu_device, case, layout):
+    B, T, N, K, H, dtype, prior = case
+    run = run_case(B, T, N, K, H, dtype, prior, layout=layout, seed=100 + B * 7 + T)
+    compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("case", [SMALL[3], SMALL[9], SMALL[0]], ids=_ids([SMALL[3], SMALL[9], SMALL[0]]))
+def test_attention_16bit_output_within_one_ulp(gpu_device, case):
+    B, T, N, K, H, dtype, prior = case
+    run = run_case(B, T, N, K, H, dtype, prior, seed=55, out_dtype=dtype)
+    G = N // K
+    worst = 0
+    for b, k in all_units(run.inp):
+        o_ref, _ = oracle_unit(run.inp, b, k, run.scale)
+        got = run.out[b, :, k * G : (k + 1) * G, :]
+        worst = max(worst, ulp_distance_16(got, o_ref, dtype))
+    say(f"  max ulp distance {worst}")
+    assert worst <= 1
+
+
+@pytest.mark.parametrize("nwg", [1, 2, 3, 7, 0, 5000])
+@pytest.mark.parametrize("T,N,K", [(1, 32, 8), (5, 64, 8)])
+def test_any_workgroup_count_gives_the_same_function(gpu_device, nwg, T, N, K):
+    run = run_case(3, T, N, K, 128, BF, [700, 65, 2000], seed=77, num_workgroups=nwg)
+    compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 32, 8), (5, 64, 8), (3, 6, 2)])
+def test_paged_equals_contiguous_bitwise(gpu_device, T, N, K):
+    kw = dict(B=4, T=T, N=N, K=K, H=128, dtype=BF, prior=[1, 200, 1500, 64], seed=78,
+              num_workgroups=37)
+    a = run_case(layout="contiguous", **kw)
+    b = run_case(layout="paged", **kw)
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.lse, b.lse)
+
+
+def test_run_twice_bitwise(gpu_device):
+    kw = dict(B=5, T=1, N=32, K=8, H=128, dtype=BF, prior=[512, 700, 64, 1025, 3], seed=79)
+    a = run_case(**kw)
+    b = run_case(**kw)
+    assert torch.equal(a.out, b.out) and torch.equal(a.lse, b.lse)
+
+
+def test_scale_one_and_large_scores(gpu_device):
+    """The pages' literal product (no scale) with N(0,1) inputs at H = 128 gives
+    scores with sd ~ 11: the softmax is nearly one-hot."""
+    run = run_case(2, 1, 8, 2, 128, BF, [300, 999], seed=80, scale=1.0)
+    compare_units(run, all_units(run.inp))
+
+
+def test_aliased_block_table_matches_copied_blocks(gpu_device):
+    """Two sequences share their prefix blocks (copy-on-write prefix sharing);
+    the result equals a run where the shared blocks are separate copies."""
+    dev = gpu_device
+    B, T, N, K, H, bs = 2, 1, 8, 2, 128, 16
+    prior = np.array([100, 100])
+    inp = draw_inputs(B, T, N, K, H, BF, prior, seed=81, device=dev)
+    # make sequence 1's first 96 prior rows identical to sequence 0's (6 full blocks)
+    inp.ctx_k[100:196] = inp.ctx_k[0:96]
+    inp.ctx_v[100:196] = inp.ctx_v[0:96]
+    seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(dev)
+    table, nb = make_block_table(3, inp.seq_lens, bs)
+    pk, pv = layout_paged(inp, table, nb, bs)
+    shared = table.copy()
+    shared[1, :6] = table[0, :6]  # point sequence 1's prefix at sequence 0's blocks
+    L = int(inp.seq_lens.max())
+    outs = []
+    for tb in (table, shared):
+        c = kvc.Cache(pk.clone(), pv.clone(), torch.from_numpy(tb).to(dev))
+        kvc.append(c, inp.k_new, inp.v_new, seq_lens)
+        outs.append(kvc.decode(inp.q[:, 0].contiguous(), c, seq_lens, L, out_dtype=torch.float32,
+                               num_workgroups=5))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_invalid_lengths_give_nan_rows_only(gpu_device):
+    dev = gpu_device
+    B, T, N, K, H = 4, 2, 8, 2, 128
+    prior = np.array([30, 40, 50, 60])
+    inp = draw_inputs(B, T, N, K, H, BF, prior, seed=82, device=dev)
+    ck, cv = layout_contiguous(inp, capacity=64)
+    cache = kvc.Cache(ck, cv)
+    lens = inp.seq_lens.astype(np.int32).copy()
+    lens[1] = 1          # < T
+    lens[3] = 65         # > capacity
+    seq_lens = torch.from_numpy(lens).to(dev)
+    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+    out, lse = kvc.verify(inp.q, cache, seq_lens, 64, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all() and torch.isnan(out[3]).all()
+    assert torch.isnan(lse[1]).all() and torch.isnan(lse[3]).all()
+    G = N // K
+    scale = 1 / math.sqrt(H)
+    for b in (0, 2):
+        for k in range(K):
+            o_ref, l_ref = oracle_unit(inp, b, k, scale)
+            got = out[b, :, k * G : (k + 1) * G].double().cpu().numpy()
+            assert np.abs(got - o_ref).max() <= 2e-3
+
+
+def test_out_of_range_block_entry_gives_nan_for_that_sequence(gpu_device):
+    dev = gpu_device
+    B, T, N, K, H = 3, 1, 8, 2, 128
+    prior = np.array([40, 40, 40])
+    inp = draw_inputs(B, T, N, K, H, BF, prior, seed=83, device=dev)
+    table, nb = make_block_table(4, inp.seq_lens, 16)
+    pk, pv = layout_paged(inp, table, nb, 16)
+    seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(dev)
+    cache = kvc.Cache(pk, pv, torch.from_numpy(table).to(dev))
+    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+    bad = table.copy()
+    bad[1, 1] = nb + 1000
+    cache_bad = kvc.Cache(pk, pv, torch.from_numpy(bad).to(dev))
+    out = kvc.decode(inp.q[:, 0].contiguous(), cache_bad, seq_lens, 41, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all()
+    assert torch.isfinite(out[0]).all() and torch.isfinite(out[2]).all()
+
+
+def test_zero_batch_is_a_noop(gpu_device):
+    ck = torch.zeros((1, 2, 16, 64), dtype=HF, device=gpu_device)
+    q = torch.zeros((0, 4, 64), dtype=HF, device=gpu_device)
+    sl = torch.zeros((0,), dtype=torch.int32, device=gpu_device)
+    out = kvc.decode(q, kvc.Cache(ck, ck.clone()), sl, 1)
+    assert out.shape == (0, 4, 64)
