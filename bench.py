@@ -115,9 +115,11 @@ def cpu_baseline(w, prior, seed, budget_s):
     done_bytes = 0
     units = 0
     elapsed = 0.0
-    b = 0
-    while elapsed < budget_s and b < w.B:
-        one = draw_inputs(1, w.T, w.N, w.K, w.H, w.dtype, prior[b : b + 1], seed + 1000 + b, device="cpu")
+    n = 0
+    while elapsed < budget_s:
+        b = n % w.B
+        one = draw_inputs(1, w.T, w.N, w.K, w.H, w.dtype, prior[b : b + 1], seed + 1000 + n, device="cpu")
+        n += 1
         kb, vb = logical_kv(one, 0)
         for k in range(w.K):
             kk = kb[:, k : k + 1].double().numpy()
@@ -130,7 +132,6 @@ def cpu_baseline(w, prior, seed, budget_s):
             units += 1
             if elapsed >= budget_s:
                 break
-        b += 1
     del torch
     return {
         "value": done_bytes / elapsed / 1e9,

@@ -73,6 +73,10 @@ typedef enum {
 
 typedef enum { KVC_F16 = 0, KVC_BF16 = 1, KVC_F32 = 2 } kvc_dtype;
 
+/* Per-unit counters at the start of every attention workspace (see
+ * kvc_attn_decode). */
+#define KVC_WORKSPACE_COUNTERS (1 << 18)
+
 /*
  * One layer's key cache and value cache (same layout, same dtype).
  *
@@ -124,7 +128,8 @@ typedef struct kvc_cache {
  * unchanged (bit-exact). Nothing else in the cache is written.
  * Errors: KVC_ERR_INVALID for null pointers, B < 0, T < 1, K < 1, bad
  * strides or alignment; KVC_ERR_UNSUPPORTED for H not in {64, 128} or a
- * dtype other than f16/bf16. B == 0 succeeds and launches nothing.
+ * dtype other than f16/bf16. B == 0 succeeds and launches nothing (the
+ * row and length pointers may then be NULL).
  */
 kvc_status kvc_append(const kvc_cache *cache, const void *k_new, const void *v_new, int B, int T,
                       int K, int H, const int32_t *seq_lens, void *stream);
@@ -142,12 +147,16 @@ kvc_status kvc_append(const kvc_cache *cache, const void *k_new, const void *v_n
  * num_workgroups: how many workgroups share the work (0 = automatic); the
  * result is the same function for every value, up to fp32 rounding order.
  * workspace: device scratch of at least kvc_workspace_bytes(B, 1, N, K, H,
- * max_seq_len, num_workgroups) bytes, ZERO-FILLED when first allocated; every
- * call leaves it zero-filled again, so it may be reused by later calls on
- * the same stream. Calls that overlap in time must not share a workspace.
+ * max_seq_len, num_workgroups) bytes, 16-byte aligned. Its first
+ * KVC_WORKSPACE_COUNTERS * 4 bytes hold per-unit counters: they must be zero
+ * when the buffer is first used, and every call that completes leaves them
+ * zero again, so one buffer may serve later calls of any shape on the same
+ * stream (the rest is scratch that each call writes before reading). Calls
+ * that overlap in time must not share a workspace.
  * Errors: as kvc_append, plus KVC_ERR_INVALID for N < 1, N % K != 0,
- * max_seq_len out of range; KVC_ERR_WORKSPACE for a missing or small
- * workspace.
+ * max_seq_len out of range; KVC_ERR_UNSUPPORTED for B > 4096 or more than
+ * KVC_WORKSPACE_COUNTERS units (B * K * ceil(G * T / 64)); KVC_ERR_WORKSPACE
+ * for a missing, misaligned or small workspace.
  */
 kvc_status kvc_attn_decode(const kvc_cache *cache, const void *q, void *out, int out_dtype,
                            float *lse, int B, int N, int K, int H, const int32_t *seq_lens,

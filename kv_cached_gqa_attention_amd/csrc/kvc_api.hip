@@ -25,6 +25,11 @@ constexpr int MIN_TILES_PER_WG = 4;    // do not spread fewer tiles over a workg
 constexpr int VALU_WG_PER_CU = 4;
 constexpr int MFMA_WG_PER_CU = 2;
 constexpr int DEFAULT_CUS = 256;
+// The workspace starts with a fixed-size array of per-unit counters. Only the
+// counter atomics (and their reset to zero by the merging workgroup) ever
+// write it, so it stays zero between calls whatever shapes they have; the
+// partials that follow are scratch, always written before being read.
+constexpr int64_t COUNTER_SLOTS = KVC_WORKSPACE_COUNTERS;
 
 int device_cu_count() {
   static int cached[64];
@@ -48,7 +53,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct Plan {
   bool mfma;
   int R, RB, RMAX, units, W;
-  size_t off_ml, off_cnt, bytes;
+  size_t off_o, off_ml, bytes;
 };
 
 bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, Plan* p) {
@@ -69,7 +74,7 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
     p->RMAX = nb * 16;
   }
   const int64_t units = (int64_t)B * K * p->RB;
-  if (units > (1 << 24)) return false;
+  if (units > COUNTER_SLOTS) return false;
   p->units = (int)units;
   if (num_wg > 0) {
     p->W = num_wg > (1 << 20) ? (1 << 20) : num_wg;
@@ -81,9 +86,9 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
     p->W = (int)(want < 1 ? 1 : want);
   }
   const size_t slots = (size_t)p->W + (size_t)p->units;
-  p->off_ml = align_up(slots * p->RMAX * H * sizeof(float), 256);
-  p->off_cnt = p->off_ml + align_up(slots * p->RMAX * 2 * sizeof(float), 256);
-  p->bytes = p->off_cnt + align_up((size_t)p->units * sizeof(int32_t), 256);
+  p->off_ml = (size_t)COUNTER_SLOTS * sizeof(int32_t);
+  p->off_o = p->off_ml + align_up(slots * p->RMAX * 2 * sizeof(float), 256);
+  p->bytes = p->off_o + align_up(slots * p->RMAX * H * sizeof(float), 256);
   return true;
 }
 
@@ -125,14 +130,15 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   int capacity = 0, shift = 0;
   const kvc_status st = check_cache(c, K, H, &capacity, &shift);
   if (st != KVC_OK) return st;
-  if (!q || !out || !seq_lens) return KVC_ERR_INVALID;
   if (B < 0 || T < 1 || T > 16 || N < 1 || N % K || num_wg < 0) return KVC_ERR_INVALID;
   if (out_dtype != KVC_F16 && out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
   if (max_seq_len < T || max_seq_len > capacity) return KVC_ERR_INVALID;
   if (!isfinite(scale)) return KVC_ERR_INVALID;
-  if (!aligned16(q)) return KVC_ERR_INVALID;
   if (B > MAX_B) return KVC_ERR_UNSUPPORTED;
-  if (B == 0) return KVC_OK;
+  if (B == 0) return KVC_OK;  // nothing to read or write; empty buffers may be null
+  if (!q || !out || !seq_lens) return KVC_ERR_INVALID;
+  if (!aligned16(q)) return KVC_ERR_INVALID;
+  if ((int64_t)B * K * ((N / K * T + 63) / 64) > COUNTER_SLOTS) return KVC_ERR_UNSUPPORTED;
   Plan p;
   if (!make_plan(B, T, N, K, H, max_seq_len, num_wg, &p)) return KVC_ERR_INVALID;
   if (!ws || ws_bytes < p.bytes || !aligned16(ws)) return KVC_ERR_WORKSPACE;
@@ -165,9 +171,9 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   a.W = p.W;
   a.scale_log2 = scale * 1.4426950408889634f;
   char* w = static_cast<char*>(ws);
-  a.part_o = reinterpret_cast<float*>(w);
+  a.counters = reinterpret_cast<int32_t*>(w);
   a.part_ml = reinterpret_cast<float*>(w + p.off_ml);
-  a.counters = reinterpret_cast<int32_t*>(w + p.off_cnt);
+  a.part_o = reinterpret_cast<float*>(w + p.off_o);
 
   const bool bf = c->dtype == KVC_BF16;
   const bool paged = c->block_table != nullptr;
@@ -186,9 +192,10 @@ kvc_status kvc_append(const kvc_cache* cache, const void* k_new, const void* v_n
   int capacity = 0, shift = 0;
   const kvc_status st = check_cache(cache, K, H, &capacity, &shift);
   if (st != KVC_OK) return st;
-  if (!k_new || !v_new || !seq_lens || B < 0 || T < 1) return KVC_ERR_INVALID;
+  if (B < 0 || T < 1) return KVC_ERR_INVALID;
+  if (B == 0) return KVC_OK;  // empty buffers may be null
+  if (!k_new || !v_new || !seq_lens) return KVC_ERR_INVALID;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVC_ERR_INVALID;
-  if (B == 0) return KVC_OK;
   CopyArgs a;
   memset(&a, 0, sizeof(a));
   a.k = static_cast<char*>(cache->k);
@@ -250,10 +257,10 @@ kvc_status kvc_gather(const kvc_cache* paged, void* dst_k, void* dst_v, int B, i
   int capacity = 0, shift = 0;
   const kvc_status st = check_cache(paged, K, H, &capacity, &shift);
   if (st != KVC_OK) return st;
-  if (!paged->block_table || !dst_k || !dst_v || !seq_lens || B < 0 || max_seq_len < 1)
-    return KVC_ERR_INVALID;
+  if (!paged->block_table || B < 0 || max_seq_len < 1) return KVC_ERR_INVALID;
+  if (B == 0) return KVC_OK;  // empty buffers may be null
+  if (!dst_k || !dst_v || !seq_lens) return KVC_ERR_INVALID;
   if (!aligned16(dst_k) || !aligned16(dst_v)) return KVC_ERR_INVALID;
-  if (B == 0) return KVC_OK;
   CopyArgs a;
   memset(&a, 0, sizeof(a));
   a.k = static_cast<char*>(paged->k);

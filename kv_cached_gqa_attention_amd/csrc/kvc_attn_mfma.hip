@@ -146,6 +146,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
       }
     };
 
+    uint4 kf[2][KS], vf[MH];
     floatx4 ot[MH][NB];
 #pragma unroll
     for (int mh = 0; mh < MH; ++mh)
@@ -158,18 +159,28 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
       l[nb] = 0.f;
     }
 
-    uint4 kf[2][KS], vf[MH];
-    int ti = s.t_begin + wave;
-    if (ti < s.t_end) {
+    auto load_k = [&](int tile) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int64_t off = row_off(ti * TILE + mb * 16 + c);
+        const int64_t off = row_off(tile * TILE + mb * 16 + c);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kf[mb][ks] = load16(kb + off + (ks * 32 + g * 8) * 2);
       }
-      const int64_t offv = row_off(ti * TILE + vtok);
+    };
+    auto load_v = [&](int tile) {
+      const int64_t offv = row_off(tile * TILE + vtok);
 #pragma unroll
       for (int mh = 0; mh < MH; ++mh) vf[mh] = load16(vb + offv + (mh * 16 + hb * 8) * 2);
+    };
+    // Loads are unconditional (clamped to the segment's last tile) so that
+    // every path into the loop leaves the same loads in flight.
+    int ti = s.t_begin + wave;
+    {
+      const int t0 = min(ti, s.t_end - 1);
+      load_k(t0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(t0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     for (; ti < s.t_end; ti += WAVES) {
@@ -185,16 +196,9 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
           st[mb][nb] = acc;
         }
 
-      // ---- next tile's K
-      const int tn = ti + WAVES;
-      if (tn < s.t_end) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int64_t off = row_off(tn * TILE + mb * 16 + c);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kf[mb][ks] = load16(kb + off + (ks * 32 + g * 8) * 2);
-        }
-      }
+      // ---- next tile's K (past the segment: its last tile again, cached)
+      const int tn = min(ti + WAVES, s.t_end - 1);
+      load_k(tn);
 
       // ---- scale, mask, online softmax (one query row per lane column)
       const int tok0 = ti * TILE;
@@ -255,11 +259,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
       }
 
       // ---- next tile's V
-      if (tn < s.t_end) {
-        const int64_t offv = row_off(tn * TILE + vtok);
-#pragma unroll
-        for (int mh = 0; mh < MH; ++mh) vf[mh] = load16(vb + offv + (mh * 16 + hb * 8) * 2);
-      }
+      load_v(tn);
     }
 
     // ---- per-column totals of l (lanes of one column hold different tokens)

@@ -63,23 +63,22 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
       const char* qrow = a.q + row_index(a, s.b, s.k, r) * (H * 2);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const uint4 v = load16(qrow + (c * SLICE + li * 8) * 2);
+        const uint4 v = load16(qrow + c * SLICE * 2 + li * 16);
         qp[r][c * 4 + 0] = v.x;
         qp[r][c * 4 + 1] = v.y;
         qp[r][c * 4 + 2] = v.z;
         qp[r][c * 4 + 3] = v.w;
       }
     }
-    // Row r = t * G + g sees keys j < vis[r] = seq_len - T + t + 1.
-    int vis[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) vis[r] = s.seq_len - a.T + r / a.G + 1;
+    // Row r = t * G + g sees keys j < seq_len - T + t + 1; only tiles that
+    // reach past vis_min need the mask.
     const int vis_min = s.seq_len - a.T + 1;
 
     const char* kb = a.k + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
     const char* vb = a.v + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
     const int32_t* trow = PAGED ? a.table + (int64_t)s.b * a.max_blocks : nullptr;
     const int bmask = (1 << a.block_shift) - 1;
+    const int lane_off = li * 16;  // byte offset of this lane's first 8 dims
     bool bad = false;
 
     // Byte offset of token `tok` (clamped to the last valid row) within head k.
@@ -91,9 +90,17 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
           bad = true;
           blk = 0;
         }
-        return (int64_t)blk * a.stride_seq + (int64_t)(tok & bmask) * a.stride_tok;
+        return (int64_t)blk * a.stride_seq + (int64_t)(tok & bmask) * a.stride_tok + lane_off;
       } else {
-        return (int64_t)tok * a.stride_tok;
+        return (int64_t)tok * a.stride_tok + lane_off;
+      }
+    };
+    auto load_rows = [&](const char* base, int tile, uint4 (&dst)[RPG][NCH]) {
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) {
+        const char* p = base + row_off(tile * TILE + grp + GROUPS * i);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) dst[i][c] = load16(p + c * SLICE * 2);
       }
     };
 
@@ -106,18 +113,18 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
       for (int d = 0; d < DPL; ++d) o[r][d] = 0.f;
     }
 
+    // First tile: issued unconditionally (a wave without tiles in this
+    // segment re-reads its last one and never uses it) and in the loop's
+    // order, all K rows then all V rows, so that every path into the loop
+    // leaves the same loads in flight and q.k waits only for K.
     uint4 kr[RPG][NCH], vr[RPG][NCH];
     int ti = s.t_begin + wave;
-    if (ti < s.t_end) {
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        const int64_t off = row_off(ti * TILE + grp + GROUPS * i);
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          kr[i][c] = load16(kb + off + (c * SLICE + li * 8) * 2);
-          vr[i][c] = load16(vb + off + (c * SLICE + li * 8) * 2);
-        }
-      }
+    {
+      const int t0 = min(ti, s.t_end - 1);
+      load_rows(kb, t0, kr);
+      __builtin_amdgcn_sched_barrier(0);
+      load_rows(vb, t0, vr);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     for (; ti < s.t_end; ti += WAVES) {
@@ -138,22 +145,16 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
           sc[r][i] = acc;
         }
       }
+      // ---- next tile's K goes out as soon as this tile's K is consumed.
+      // The prefetch is unconditional (no register copies for a conditional
+      // load); past the segment it re-reads the segment's last tile, which
+      // this workgroup has just brought into the cache.
+      const int tn = min(ti + WAVES, s.t_end - 1);
+      load_rows(kb, tn, kr);
 #pragma unroll
       for (int i = 0; i < RPG; ++i)
 #pragma unroll
         for (int r = 0; r < R; ++r) sc[r][i] = group_sum<LPR>(sc[r][i]) * a.scale_log2;
-
-      // ---- next tile's K
-      const int tn = ti + WAVES;
-      int64_t offn[RPG];
-      if (tn < s.t_end) {
-#pragma unroll
-        for (int i = 0; i < RPG; ++i) {
-          offn[i] = row_off(tn * TILE + grp + GROUPS * i);
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) kr[i][c] = load16(kb + offn[i] + (c * SLICE + li * 8) * 2);
-        }
-      }
 
       // ---- causal / length mask (only the last tiles of a sequence)
       const int tok0 = ti * TILE;
@@ -163,24 +164,33 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
           const int tok = tok0 + grp + GROUPS * i;
 #pragma unroll
           for (int r = 0; r < R; ++r)
-            if (tok >= vis[r]) sc[r][i] = -INFINITY;
+            if (tok >= vis_min + r / a.G) sc[r][i] = -__builtin_inff();
         }
       }
 
-      // ---- online softmax
+      // ---- online softmax; the rescale runs only when some row's max grew
+      float mn[R];
+      bool grew = false;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float mt = sc[r][0];
 #pragma unroll
         for (int i = 1; i < RPG; ++i) mt = fmaxf(mt, sc[r][i]);
-        const float mn = fmaxf(m[r], mt);
-        if (mn > m[r]) {
-          const float alpha = __builtin_amdgcn_exp2f(m[r] - mn);
+        mn[r] = fmaxf(m[r], mt);
+        grew |= mn[r] > m[r];
+      }
+      if (__builtin_amdgcn_ballot_w64(grew) != 0ull) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float alpha = __builtin_amdgcn_exp2f(m[r] - mn[r]);
           l[r] *= alpha;
 #pragma unroll
           for (int d = 0; d < DPL; ++d) o[r][d] *= alpha;
-          m[r] = mn;
+          m[r] = mn[r];
         }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {
           const float p = __builtin_amdgcn_exp2f(sc[r][i] - m[r]);
@@ -207,14 +217,8 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
           }
         }
       }
-
       // ---- next tile's V
-      if (tn < s.t_end) {
-#pragma unroll
-        for (int i = 0; i < RPG; ++i)
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) vr[i][c] = load16(vb + offn[i] + (c * SLICE + li * 8) * 2);
-      }
+      load_rows(vb, tn, vr);
     }
 
     // ---- combine the lane groups of this wave

@@ -117,6 +117,24 @@ __device__ __forceinline__ uint4 load16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Device-coherent scalar store / load (device-scope relaxed atomics: they
+// bypass a stale or dirty copy in this XCD's L2).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding vector memory operations (stores
+// included) are acknowledged: s_waitcnt vmcnt(0), leaving the LDS and export
+// counters alone. The signal fences keep the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- cross-lane
 
 // DPP controls (GFX9 encoding).
@@ -341,43 +359,49 @@ __device__ void finish_segment(const AttnArgs& a, const Segment& s, const float*
       O += sc * s_o[(w * a.RMAX + r) * H + h];
     }
     if (bad) O = L = M = qnan;
-    po[r * H + h] = O;
+    store_coherent(po + r * H + h, O);
     if (h == 0) {
-      pml[r * 2 + 0] = M;
-      pml[r * 2 + 1] = L;
+      store_coherent(pml + r * 2 + 0, M);
+      store_coherent(pml + r * 2 + 1, L);
     }
   }
-  // Release the partial to other workgroups (other XCDs included), then count.
-  __threadfence();
+  // Publish the partial, then count it. The partial's stores are device-
+  // coherent (they bypass this XCD's L2 copy), so waiting for their
+  // acknowledgement before the barrier is the whole release: no L2-wide
+  // write-back or invalidate is needed.
+  wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&a.counters[s.unit], 1);
+    const int prev = __hip_atomic_fetch_add(&a.counters[s.unit], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
     s_flag[0] = (prev == s.n_parts - 1);
   }
   __syncthreads();
   if (s_flag[0]) {
-    __threadfence();  // acquire the other workgroups' partials
+    // Every other partial of the unit was acknowledged before its counter
+    // increment, which preceded ours; device-coherent loads see them.
     for (int e = threadIdx.x; e < rows * H; e += THREADS) {
       const int r = e / H, h = e - (e / H) * H;
       float M = NEG_BIG;
       for (int i = 0; i < s.n_parts; ++i) {
         const float* ml = a.part_ml + (int64_t)(s.first_wg + i + s.unit) * a.RMAX * 2;
-        M = fmaxf(M, ml[r * 2]);
+        M = fmaxf(M, load_coherent(ml + r * 2));
       }
       float L = 0.f, O = 0.f;
       for (int i = 0; i < s.n_parts; ++i) {
         const int64_t sl = s.first_wg + i + s.unit;
         const float* ml = a.part_ml + sl * a.RMAX * 2;
-        const float mi = ml[r * 2];
-        const float li = ml[r * 2 + 1];
-        const float oi = a.part_o[(sl * a.RMAX + r) * H + h];
+        const float mi = load_coherent(ml + r * 2);
+        const float li = load_coherent(ml + r * 2 + 1);
+        const float oi = load_coherent(a.part_o + (sl * a.RMAX + r) * H + h);
         const float sc = exp2f(mi - M);
         L += sc * li;
         O += sc * oi;
       }
       write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
     }
-    if (threadIdx.x == 0) atomicExch(&a.counters[s.unit], 0);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.counters[s.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }

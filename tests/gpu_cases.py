@@ -112,13 +112,3 @@ def compare_units(run, units, out_tol=TOL, lse_tol=TOL):
 
 def all_units(inp):
     return [(b, k) for b in range(inp.B) for k in range(inp.K)]
-
-
-def ulp_distance_16(got: torch.Tensor, ref64: np.ndarray, dtype) -> int:
-    """Max distance in units of the last place between 16-bit outputs and RNE(ref)."""
-    ref = torch.from_numpy(ref64).to(torch.float32).to(dtype)
-    ib = lambda t: t.contiguous().view(torch.int16).to(torch.int32).numpy()
-    a, r = ib(got.cpu()), ib(ref)
-    # map sign-magnitude to a monotone integer line
-    mono = lambda x: np.where(x < 0, -(x & 0x7FFF), x)
-    return int(np.abs(mono(a) - mono(r)).max())

@@ -102,6 +102,7 @@ def test_decode_host_errors(lib):
     assert _decode(lib, _cache(), max_seq_len=0) == E.KVC_ERR_INVALID
     assert _decode(lib, _cache(), out_dtype=9) == E.KVC_ERR_UNSUPPORTED
     assert _decode(lib, _cache(), q=FAKE + 2) == E.KVC_ERR_INVALID
+    assert _decode(lib, _cache(), B=0, max_seq_len=4097) == E.KVC_ERR_INVALID
     assert _decode(lib, _cache(), q=None) == E.KVC_ERR_INVALID
     assert _decode(lib, _cache(), seq_lens=None) == E.KVC_ERR_INVALID
     assert _decode(lib, _cache(stride_tok=100)) == E.KVC_ERR_INVALID
@@ -111,8 +112,9 @@ def test_decode_host_errors(lib):
     assert _decode(lib, _cache(), B=5000) == E.KVC_ERR_UNSUPPORTED
     assert _decode(lib, _cache(), ws=None) == E.KVC_ERR_WORKSPACE
     assert _decode(lib, _cache(), ws_bytes=16) == E.KVC_ERR_WORKSPACE
-    # B == 0 is a successful no-op (nothing launched)
+    # B == 0 is a successful no-op (nothing launched; empty buffers may be null)
     assert _decode(lib, _cache(), B=0) == E.KVC_OK
+    assert _decode(lib, _cache(), B=0, q=None, seq_lens=None) == E.KVC_OK
 
 
 def test_paged_descriptor_errors(lib):

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import kv_cached_gqa_attention_amd as kvc
-from gpu_cases import all_units, compare_units, oracle_unit, run_case, say, ulp_distance_16
+from gpu_cases import all_units, compare_units, oracle_unit, run_case, say
 from workloads import draw_inputs, layout_contiguous, layout_paged, logical_kv, make_block_table
 
 pytestmark = pytest.mark.gpu
@@ -111,17 +111,26 @@ def test_attention_parity_fp32(gpu_device, case, layout):
 
 
 @pytest.mark.parametrize("case", [SMALL[3], SMALL[9], SMALL[0]], ids=_ids([SMALL[3], SMALL[9], SMALL[0]]))
-def test_attention_16bit_output_within_one_ulp(gpu_device, case):
+def test_attention_16bit_output(gpu_device, case):
+    """16-bit outputs: within the fp32 tolerance plus half an output ulp of the
+    oracle, and bit-equal to round-to-nearest-even of the same launch's fp32
+    result (the final rounding is exactly RNE)."""
     B, T, N, K, H, dtype, prior = case
-    run = run_case(B, T, N, K, H, dtype, prior, seed=55, out_dtype=dtype)
+    run16 = run_case(B, T, N, K, H, dtype, prior, seed=55, out_dtype=dtype, num_workgroups=19)
+    run32 = run_case(B, T, N, K, H, dtype, prior, seed=55, out_dtype=torch.float32, num_workgroups=19)
+    assert torch.equal(run16.out.view(torch.int16), run32.out.to(dtype).view(torch.int16))
     G = N // K
-    worst = 0
-    for b, k in all_units(run.inp):
-        o_ref, _ = oracle_unit(run.inp, b, k, run.scale)
-        got = run.out[b, :, k * G : (k + 1) * G, :]
-        worst = max(worst, ulp_distance_16(got, o_ref, dtype))
-    say(f"  max ulp distance {worst}")
-    assert worst <= 1
+    mant = 7 if dtype is BF else 10
+    worst = 0.0
+    for b, k in all_units(run16.inp):
+        o_ref, _ = oracle_unit(run16.inp, b, k, run16.scale)
+        got = run16.out[b, :, k * G : (k + 1) * G, :].double().cpu().numpy()
+        mag = np.maximum(np.abs(o_ref), 2.0 ** -126)
+        half_ulp = 0.5 * 2.0 ** (np.floor(np.log2(mag)) - mant)
+        excess = np.abs(got - o_ref) - half_ulp
+        worst = max(worst, float(excess.max()))
+    say(f"  16-bit: max(|d| - ulp/2) = {worst:.3e}")
+    assert worst <= 2e-3
 
 
 @pytest.mark.parametrize("nwg", [1, 2, 3, 7, 0, 5000])
@@ -231,3 +240,32 @@ def test_zero_batch_is_a_noop(gpu_device):
     sl = torch.zeros((0,), dtype=torch.int32, device=gpu_device)
     out = kvc.decode(q, kvc.Cache(ck, ck.clone()), sl, 1)
     assert out.shape == (0, 4, 64)
+
+
+def test_one_workspace_serves_calls_of_any_shape(gpu_device):
+    """Regression: calls of different shapes share one workspace; the counter
+    region they all use must stay zero between calls."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=gpu_device)
+    shapes = [
+        (2, 1, 16, 2, 128, BF, [33, 97]),   # R = 8, wide partial rows
+        (2, 1, 4, 2, 64, HF, [33, 97]),     # R = 2, narrow
+        (2, 5, 64, 8, 128, BF, [100, 555]), # matrix cores
+        (3, 1, 8, 8, 128, BF, [0, 31, 200]),
+    ]
+    for rep in range(2):
+        for B, T, N, K, H, dtype, prior in shapes:
+            from gpu_cases import build_cache
+
+            inp = draw_inputs(B, T, N, K, H, dtype, np.array(prior), seed=90 + rep, device=gpu_device)
+            cache, _ = build_cache(inp, "contiguous", 90)
+            sl = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(gpu_device)
+            kvc.append(cache, inp.k_new, inp.v_new, sl)
+            L = int(inp.seq_lens.max())
+            out = kvc.verify(inp.q, cache, sl, L, out_dtype=torch.float32, ws=ws)
+            torch.cuda.synchronize()
+            G = N // K
+            for b in range(B):
+                for k in range(K):
+                    o_ref, _ = oracle_unit(inp, b, k, 1 / math.sqrt(H))
+                    got = out[b, :, k * G : (k + 1) * G].double().cpu().numpy()
+                    assert np.abs(got - o_ref).max() <= 2e-3, (rep, B, T, N, K, H)
