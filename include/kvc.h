@@ -139,7 +139,7 @@ kvc_status kvc_append(const kvc_cache *cache, const void *k_new, const void *v_n
  * kvc_attn_verify with T = 1.
  *
  * q: [B, N, H] in cache->dtype. out: [B, N, H] in out_dtype (f32, f16 or
- * bf16; 16-bit outputs are rounded to nearest even). lse: [B, N] fp32, or
+ * bf16, 16-byte aligned; 16-bit outputs are rounded to nearest even). lse: [B, N] fp32, or
  * NULL. max_seq_len (host) is an upper bound on seq_lens[] used only to size
  * the launch (a longer device length is still computed correctly, just with
  * fewer workgroups than ideal); it must satisfy 1 <= max_seq_len <= capacity.

@@ -19,11 +19,16 @@ using kvc::AttnArgs;
 using kvc::CopyArgs;
 
 constexpr int MAX_B = 4096;            // sequences per call (per-workgroup LDS prefix table)
-constexpr int VALU_MAX_ROWS = 8;       // G * T up to this uses the vector-ALU kernel
+// G * T up to this uses the vector-ALU kernel (its per-lane state grows with
+// the rows); more rows go to the matrix cores.
+constexpr int valu_max_rows(int H) { return H == 64 ? 8 : 4; }
 constexpr int MFMA_MAX_NB = 4;         // 16-row blocks per matrix-core unit
-constexpr int MIN_TILES_PER_WG = 4;    // do not spread fewer tiles over a workgroup
-constexpr int VALU_WG_PER_CU = 4;
-constexpr int MFMA_WG_PER_CU = 2;
+constexpr int MIN_STEPS_PER_WORKER = 2;  // do not spread fewer 128-token steps over a workgroup
+// Resident workgroups per CU at the kernels' register use (vector-ALU kernel:
+// 2 waves per SIMD; matrix-core kernel: 1), so an automatic grid is one
+// round of workgroups.
+constexpr int VALU_WG_PER_CU = 2;
+constexpr int MFMA_WG_PER_CU = 1;
 constexpr int DEFAULT_CUS = 256;
 // The workspace starts with a fixed-size array of per-unit counters. Only the
 // counter atomics (and their reset to zero by the merging workgroup) ever
@@ -52,7 +57,9 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
   bool mfma;
-  int R, RB, RMAX, units, W;
+  int R, RB, RMAX, units;
+  int W;        // workgroups launched
+  int workers;  // independent workers: waves (vector-ALU kernel) or workgroups (matrix cores)
   size_t off_o, off_ml, bytes;
 };
 
@@ -62,7 +69,7 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
     return false;
   const int G = N / K;
   p->R = G * T;
-  if (p->R <= VALU_MAX_ROWS) {
+  if (p->R <= valu_max_rows(H)) {
     p->mfma = false;
     p->RB = 1;
     p->RMAX = p->R;
@@ -76,16 +83,19 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
   const int64_t units = (int64_t)B * K * p->RB;
   if (units > COUNTER_SLOTS) return false;
   p->units = (int)units;
+  const int per_wg = 1;  // both kernels: one worker per workgroup
   if (num_wg > 0) {
     p->W = num_wg > (1 << 20) ? (1 << 20) : num_wg;
   } else {
-    const int64_t tiles_ub = units * ((max_seq_len + kvc::TILE - 1) / kvc::TILE);
+    const int64_t steps_ub = units * ((max_seq_len + kvc::STEP - 1) / kvc::STEP);
     const int64_t full = (int64_t)device_cu_count() * (p->mfma ? MFMA_WG_PER_CU : VALU_WG_PER_CU);
-    int64_t want = (tiles_ub + MIN_TILES_PER_WG - 1) / MIN_TILES_PER_WG;
+    const int64_t want_workers = (steps_ub + MIN_STEPS_PER_WORKER - 1) / MIN_STEPS_PER_WORKER;
+    int64_t want = (want_workers + per_wg - 1) / per_wg;
     if (want > full) want = full;
     p->W = (int)(want < 1 ? 1 : want);
   }
-  const size_t slots = (size_t)p->W + (size_t)p->units;
+  p->workers = p->W * per_wg;
+  const size_t slots = (size_t)p->workers + (size_t)p->units;
   p->off_ml = (size_t)COUNTER_SLOTS * sizeof(int32_t);
   p->off_o = p->off_ml + align_up(slots * p->RMAX * 2 * sizeof(float), 256);
   p->bytes = p->off_o + align_up(slots * p->RMAX * H * sizeof(float), 256);
@@ -137,7 +147,7 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   if (B > MAX_B) return KVC_ERR_UNSUPPORTED;
   if (B == 0) return KVC_OK;  // nothing to read or write; empty buffers may be null
   if (!q || !out || !seq_lens) return KVC_ERR_INVALID;
-  if (!aligned16(q)) return KVC_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(out)) return KVC_ERR_INVALID;
   if ((int64_t)B * K * ((N / K * T + 63) / 64) > COUNTER_SLOTS) return KVC_ERR_UNSUPPORTED;
   Plan p;
   if (!make_plan(B, T, N, K, H, max_seq_len, num_wg, &p)) return KVC_ERR_INVALID;
@@ -168,7 +178,7 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   a.RB = p.RB;
   a.RMAX = p.RMAX;
   a.out_dtype = out_dtype;
-  a.W = p.W;
+  a.W = p.workers;
   a.scale_log2 = scale * 1.4426950408889634f;
   char* w = static_cast<char*>(ws);
   a.counters = reinterpret_cast<int32_t*>(w);

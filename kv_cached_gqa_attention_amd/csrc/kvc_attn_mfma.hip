@@ -94,7 +94,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a);
-  const Partition part = make_partition(a, s_pre);
+  const Partition part = make_partition(a, s_pre, blockIdx.x);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -172,18 +172,15 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int mh = 0; mh < MH; ++mh) vf[mh] = load16(vb + offv + (mh * 16 + hb * 8) * 2);
     };
-    // Loads are unconditional (clamped to the segment's last tile) so that
-    // every path into the loop leaves the same loads in flight.
-    int ti = s.t_begin + wave;
-    {
-      const int t0 = min(ti, s.t_end - 1);
-      load_k(t0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_v(t0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // Work comes in steps of one tile per wave, so the four waves have equal
+    // work; tiles past the unit's end are masked (their loads are clamped).
+    load_k(s.t_begin * WAVES + wave);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(s.t_begin * WAVES + wave);
+    __builtin_amdgcn_sched_barrier(0);
 
-    for (; ti < s.t_end; ti += WAVES) {
+    for (int sp = s.t_begin; sp < s.t_end; ++sp) {
+      const int ti = sp * WAVES + wave;
       // ---- S^T = K . Q^T
       floatx4 st[2][NB];
 #pragma unroll
@@ -196,8 +193,8 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
           st[mb][nb] = acc;
         }
 
-      // ---- next tile's K (past the segment: its last tile again, cached)
-      const int tn = min(ti + WAVES, s.t_end - 1);
+      // ---- next tile's K (past the segment: this tile again, cached)
+      const int tn = min(sp + 1, s.t_end - 1) * WAVES + wave;
       load_k(tn);
 
       // ---- scale, mask, online softmax (one query row per lane column)
@@ -303,7 +300,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    finish_segment<H, 1>(a, s, s_m, s_l, s_o, segbad, s_flag);
+    finish_segment<H, 1>(a, s, blockIdx.x, s_m, s_l, s_o, segbad, s_flag);
   }
 }
 
@@ -312,6 +309,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 template <bool BF, int H, int NB, bool PAGED>
 static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
   const size_t shmem = (size_t)(a.B + 1) * sizeof(int32_t);
+  // one worker per workgroup
   hipLaunchKernelGGL((attn_mfma_kernel<BF, H, NB, PAGED>), dim3(a.W), dim3(THREADS), shmem, stream, a);
   return hipGetLastError();
 }

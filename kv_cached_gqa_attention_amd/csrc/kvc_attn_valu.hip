@@ -1,6 +1,6 @@
 // Split-KV attention on the vector ALUs, for units with few query rows
-// (R = G * T <= 8: single-token decode with GQA groups up to 8, or short
-// verify blocks of small groups).
+// (R = G * T <= 4 at head size 128, <= 8 at head size 64: single-token
+// decode with small GQA groups, or short verify blocks of small groups).
 //
 // What it computes is the cached attention of "Making inference cheap: KV
 // cache, batching and quantization" (the new token's query against every
@@ -23,16 +23,22 @@
 //    widens V to fp32 (exact) and accumulates in fp32.
 //  * Loads are software-pipelined: the next tile's K is requested right
 //    after the current q.k, its V right after the current p.v.
+//  * A workgroup owns a contiguous range of tiles; its four waves take
+//    alternate tiles, so together they stream one contiguous window (worth
+//    about 15% of bandwidth over four far-apart streams). At a unit boundary
+//    the waves park their states in LDS, combine, and publish a partial; the
+//    next unit's first tiles are requested before that, so the stream does
+//    not drain at the boundary. Work is counted in steps of one tile per
+//    wave, so the four waves always have equal work.
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
 namespace kvc {
 
-template <bool BF, int H, int R, int LPR, bool PAGED>
-__global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
+template <bool BF, int H, int R, int LPR, bool PAGED, int WPE>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_valu_kernel(AttnArgs a) {
   constexpr int DPL = H / LPR;         // dims per lane: 8 or 16
   constexpr int NCH = DPL / 8;         // 16-byte chunks per lane per row
-  constexpr int NW32 = DPL / 2;        // packed 32-bit words per lane per row
   constexpr int GROUPS = 64 / LPR;     // rows per wave instruction
   constexpr int RPG = TILE / GROUPS;   // tokens per lane group per tile
   constexpr int SLICE = H / NCH;       // elements covered by one chunk across the group
@@ -45,64 +51,64 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
 
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a);
-  const Partition part = make_partition(a, s_pre);
+  const Partition part = make_partition(a, s_pre, blockIdx.x);
+  if (part.lo >= part.hi) return;  // the whole workgroup: no barrier is skipped
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int grp = lane / LPR;
   const int li = lane % LPR;
+  const int lane_off = li * 16;  // byte offset of this lane's first 8 dims in a row
+  const int bmask = (1 << a.block_shift) - 1;
 
-  for (int64_t x = part.lo; x < part.hi;) {
-    const Segment s = find_segment(a, s_pre, part, x);
-    x += s.t_end - s.t_begin;
-
-    // Query rows of the unit, packed, this lane's dims.
-    uint32_t qp[R][NW32];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const char* qrow = a.q + row_index(a, s.b, s.k, r) * (H * 2);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const uint4 v = load16(qrow + c * SLICE * 2 + li * 16);
-        qp[r][c * 4 + 0] = v.x;
-        qp[r][c * 4 + 1] = v.y;
-        qp[r][c * 4 + 2] = v.z;
-        qp[r][c * 4 + 3] = v.w;
+  auto kbase = [&](const Segment& g) {
+    return a.k + (int64_t)g.k * a.stride_head + (PAGED ? 0 : (int64_t)g.b * a.stride_seq);
+  };
+  auto vbase = [&](const Segment& g) {
+    return a.v + (int64_t)g.k * a.stride_head + (PAGED ? 0 : (int64_t)g.b * a.stride_seq);
+  };
+  // Byte offset of token `tok` of sequence g.b (clamped to its last valid
+  // row); an out-of-range block entry reads block 0 and flags the unit.
+  auto row_off = [&](const Segment& g, int tok, bool& bad) -> int64_t {
+    tok = min(tok, g.seq_len - 1);
+    if constexpr (PAGED) {
+      int blk = a.table[(int64_t)g.b * a.max_blocks + (tok >> a.block_shift)];
+      if ((unsigned)blk >= (unsigned)a.num_blocks) {
+        bad = true;
+        blk = 0;
       }
+      return (int64_t)blk * a.stride_seq + (int64_t)(tok & bmask) * a.stride_tok + lane_off;
+    } else {
+      return (int64_t)tok * a.stride_tok + lane_off;
     }
+  };
+  auto load_rows = [&](const char* base, const Segment& g, int tile, uint4 (&dst)[RPG][NCH],
+                       bool& bad) {
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const char* p = base + row_off(g, tile * TILE + grp + GROUPS * i, bad);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) dst[i][c] = load16(p + c * SLICE * 2);
+    }
+  };
+  Segment cur = find_segment(a, s_pre, part, part.lo);
+  int64_t x_next = part.lo + (cur.t_end - cur.t_begin);
+
+  // This wave's tile of the first step, all K rows then all V rows (the
+  // loop's issue order).
+  bool bad_cur = false, bad_nxt = false;
+  uint4 kr[RPG][NCH], vr[RPG][NCH];
+  load_rows(kbase(cur), cur, cur.t_begin * WAVES + wave, kr, bad_cur);
+  __builtin_amdgcn_sched_barrier(0);
+  load_rows(vbase(cur), cur, cur.t_begin * WAVES + wave, vr, bad_cur);
+  __builtin_amdgcn_sched_barrier(0);
+
+  while (true) {
+    const bool has_next = x_next < part.hi;
+    const Segment nxt = has_next ? find_segment(a, s_pre, part, x_next) : cur;
     // Row r = t * G + g sees keys j < seq_len - T + t + 1; only tiles that
     // reach past vis_min need the mask.
-    const int vis_min = s.seq_len - a.T + 1;
-
-    const char* kb = a.k + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
-    const char* vb = a.v + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
-    const int32_t* trow = PAGED ? a.table + (int64_t)s.b * a.max_blocks : nullptr;
-    const int bmask = (1 << a.block_shift) - 1;
-    const int lane_off = li * 16;  // byte offset of this lane's first 8 dims
-    bool bad = false;
-
-    // Byte offset of token `tok` (clamped to the last valid row) within head k.
-    auto row_off = [&](int tok) -> int64_t {
-      tok = min(tok, s.seq_len - 1);
-      if constexpr (PAGED) {
-        int blk = trow[tok >> a.block_shift];
-        if ((unsigned)blk >= (unsigned)a.num_blocks) {
-          bad = true;
-          blk = 0;
-        }
-        return (int64_t)blk * a.stride_seq + (int64_t)(tok & bmask) * a.stride_tok + lane_off;
-      } else {
-        return (int64_t)tok * a.stride_tok + lane_off;
-      }
-    };
-    auto load_rows = [&](const char* base, int tile, uint4 (&dst)[RPG][NCH]) {
-#pragma unroll
-      for (int i = 0; i < RPG; ++i) {
-        const char* p = base + row_off(tile * TILE + grp + GROUPS * i);
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) dst[i][c] = load16(p + c * SLICE * 2);
-      }
-    };
+    const int vis_min = cur.seq_len - a.T + 1;
 
     float m[R], l[R], o[R][DPL];
 #pragma unroll
@@ -112,45 +118,48 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
       for (int d = 0; d < DPL; ++d) o[r][d] = 0.f;
     }
-
-    // First tile: issued unconditionally (a wave without tiles in this
-    // segment re-reads its last one and never uses it) and in the loop's
-    // order, all K rows then all V rows, so that every path into the loop
-    // leaves the same loads in flight and q.k waits only for K.
-    uint4 kr[RPG][NCH], vr[RPG][NCH];
-    int ti = s.t_begin + wave;
-    {
-      const int t0 = min(ti, s.t_end - 1);
-      load_rows(kb, t0, kr);
-      __builtin_amdgcn_sched_barrier(0);
-      load_rows(vb, t0, vr);
-      __builtin_amdgcn_sched_barrier(0);
+    // The unit's query rows, this lane's dims (the unit's first K/V tile is
+    // already in flight, so this load adds little latency).
+    uint4 qreg[R][NCH];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const char* qrow = a.q + row_index(a, cur.b, cur.k, r) * (H * 2);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) qreg[r][c] = load16(qrow + c * SLICE * 2 + li * 16);
     }
 
-    for (; ti < s.t_end; ti += WAVES) {
+    for (int st = cur.t_begin; st < cur.t_end; ++st) {
+      const int ti = st * WAVES + wave;  // this wave's tile of step st
       // ---- scores (base 2)
       float sc[R][RPG];
 #pragma unroll
-      for (int i = 0; i < RPG; ++i) {
+      for (int r = 0; r < R; ++r) {
+        uint4 q4[NCH];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+        for (int c = 0; c < NCH; ++c) q4[c] = qreg[r][c];
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) {
           float acc = 0.f;
 #pragma unroll
           for (int c = 0; c < NCH; ++c) {
-            acc = dot2<BF>(kr[i][c].x, qp[r][c * 4 + 0], acc);
-            acc = dot2<BF>(kr[i][c].y, qp[r][c * 4 + 1], acc);
-            acc = dot2<BF>(kr[i][c].z, qp[r][c * 4 + 2], acc);
-            acc = dot2<BF>(kr[i][c].w, qp[r][c * 4 + 3], acc);
+            acc = dot2<BF>(kr[i][c].x, q4[c].x, acc);
+            acc = dot2<BF>(kr[i][c].y, q4[c].y, acc);
+            acc = dot2<BF>(kr[i][c].z, q4[c].z, acc);
+            acc = dot2<BF>(kr[i][c].w, q4[c].w, acc);
           }
           sc[r][i] = acc;
         }
       }
-      // ---- next tile's K goes out as soon as this tile's K is consumed.
-      // The prefetch is unconditional (no register copies for a conditional
-      // load); past the segment it re-reads the segment's last tile, which
-      // this workgroup has just brought into the cache.
-      const int tn = min(ti + WAVES, s.t_end - 1);
-      load_rows(kb, tn, kr);
+      // ---- this wave's next tile: in the next step of this unit, else in
+      // the next unit's first step, else this tile again (cached). Loads are
+      // unconditional: a conditional load costs register copies.
+      const bool hop = has_next && st + 1 == cur.t_end;
+      const Segment& ng = hop ? nxt : cur;
+      const int tn = (hop ? nxt.t_begin : min(st + 1, cur.t_end - 1)) * WAVES + wave;
+      const char* nkb = hop ? kbase(nxt) : kbase(cur);
+      const char* nvb = hop ? vbase(nxt) : vbase(cur);
+      bool nbad = false;
+      load_rows(nkb, ng, tn, kr, nbad);
 #pragma unroll
       for (int i = 0; i < RPG; ++i)
 #pragma unroll
@@ -218,19 +227,20 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
         }
       }
       // ---- next tile's V
-      load_rows(vb, tn, vr);
+      load_rows(nvb, ng, tn, vr, nbad);
+      if (hop) bad_nxt |= nbad; else bad_cur |= nbad;
     }
 
-    // ---- combine the lane groups of this wave
+    // ---- combine this wave's lane groups, park the wave's state in LDS
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float M = m[r];
+      float mr = m[r];
 #pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) M = fmaxf(M, shfl_xor_f(M, msk));
-      const float scl = __builtin_amdgcn_exp2f(m[r] - M);
-      float L = l[r] * scl;
+      for (int msk = LPR; msk < 64; msk <<= 1) mr = fmaxf(mr, shfl_xor_f(mr, msk));
+      const float scl = __builtin_amdgcn_exp2f(m[r] - mr);
+      float lr = l[r] * scl;
 #pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) L += shfl_xor_f(L, msk);
+      for (int msk = LPR; msk < 64; msk <<= 1) lr += shfl_xor_f(lr, msk);
 #pragma unroll
       for (int d = 0; d < DPL; ++d) {
         float od = o[r][d] * scl;
@@ -238,26 +248,35 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
         for (int msk = LPR; msk < 64; msk <<= 1) od += shfl_xor_f(od, msk);
         o[r][d] = od;
       }
-      if (grp == 0) {
+      // lane group g parks rows g, g + GROUPS, ...
+      if (r % GROUPS == grp) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) s_o[(wave * R + r) * H + c * SLICE + li * 8 + e] = o[r][c * 8 + e];
       }
       if (lane == 0) {
-        s_m[wave * R + r] = M;
-        s_l[wave * R + r] = L;
+        s_m[wave * R + r] = mr;
+        s_l[wave * R + r] = lr;
       }
     }
     {
-      const unsigned long long anybad = __ballot(bad);
+      const unsigned long long anybad = __builtin_amdgcn_ballot_w64(bad_cur);
       if (lane == 0) s_bad[wave] = anybad != 0ull;
     }
     __syncthreads();
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    finish_segment<H, WAVES>(a, s, s_m, s_l, s_o, segbad, s_flag);
+    // The next unit's first tiles are in flight while the workgroup combines
+    // and publishes this one.
+    finish_segment<H, WAVES>(a, cur, blockIdx.x, s_m, s_l, s_o, segbad, s_flag);
+
+    if (!has_next) break;
+    cur = nxt;
+    x_next += nxt.t_end - nxt.t_begin;
+    bad_cur = bad_nxt;
+    bad_nxt = false;
   }
 }
 
@@ -265,10 +284,15 @@ __global__ __launch_bounds__(THREADS) void attn_valu_kernel(AttnArgs a) {
 
 template <bool BF, int H, int R, bool PAGED>
 static hipError_t launch_valu_t(const AttnArgs& a, hipStream_t stream) {
-  constexpr int LPR = (H == 64) ? 8 : (R <= 4 ? 8 : 16);
+  constexpr int LPR = 8;
+  // Two waves per SIMD where the main loop still fits without spilling
+  // (a few spills outside the loop are cheap); otherwise let the compiler
+  // take the registers it wants.
+  constexpr int WPE = (H == 128 && R <= 4) || (H == 64 && R <= 6) ? 2 : 1;
   const size_t shmem = (size_t)(a.B + 1) * sizeof(int32_t);
-  hipLaunchKernelGGL((attn_valu_kernel<BF, H, R, LPR, PAGED>), dim3(a.W), dim3(THREADS), shmem,
-                     stream, a);
+  // one worker per workgroup; its waves interleave the tiles
+  hipLaunchKernelGGL((attn_valu_kernel<BF, H, R, LPR, PAGED, WPE>), dim3(a.W), dim3(THREADS),
+                     shmem, stream, a);
   return hipGetLastError();
 }
 
@@ -279,12 +303,18 @@ static hipError_t launch_valu_r(const AttnArgs& a, hipStream_t stream) {
     case 2: return launch_valu_t<BF, H, 2, PAGED>(a, stream);
     case 3: return launch_valu_t<BF, H, 3, PAGED>(a, stream);
     case 4: return launch_valu_t<BF, H, 4, PAGED>(a, stream);
-    case 5: return launch_valu_t<BF, H, 5, PAGED>(a, stream);
-    case 6: return launch_valu_t<BF, H, 6, PAGED>(a, stream);
-    case 7: return launch_valu_t<BF, H, 7, PAGED>(a, stream);
-    case 8: return launch_valu_t<BF, H, 8, PAGED>(a, stream);
-    default: return hipErrorInvalidValue;
+    default: break;
   }
+  if constexpr (H == 64) {
+    switch (a.R) {
+      case 5: return launch_valu_t<BF, H, 5, PAGED>(a, stream);
+      case 6: return launch_valu_t<BF, H, 6, PAGED>(a, stream);
+      case 7: return launch_valu_t<BF, H, 7, PAGED>(a, stream);
+      case 8: return launch_valu_t<BF, H, 8, PAGED>(a, stream);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_valu(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {

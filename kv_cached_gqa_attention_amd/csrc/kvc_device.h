@@ -9,6 +9,9 @@
 // workgroup takes an equal contiguous share of that flat range, computed on
 // the device from seq_lens (no host read of lengths: "Accelerating Sonar
 // through speculation", section "Inference with speculative decoding").
+// The range is counted in steps of WAVES tiles (128 tokens): a workgroup's
+// waves take one tile of each step, so they always have equal work; the last
+// step of a unit may hold tiles past its end, which are masked.
 // A workgroup whose share covers part of a unit writes an online-softmax
 // partial (m, l, o) for it; the last workgroup to finish the unit merges the
 // partials by log-sum-exp. This is the split-KV idea that "CS336, lectures 10
@@ -24,9 +27,10 @@
 
 namespace kvc {
 
-constexpr int TILE = 32;        // tokens per work tile
+constexpr int TILE = 32;        // tokens per wave iteration
 constexpr int WAVES = 4;        // waves per workgroup
 constexpr int THREADS = 64 * WAVES;
+constexpr int STEP = TILE * WAVES;  // tokens per partition step (one tile per wave)
 constexpr float NEG_BIG = -1.0e30f;  // running max before any visible key; exp2(NEG_BIG - x) == 0
 constexpr float LN2 = 0.69314718055994531f;
 
@@ -54,9 +58,9 @@ struct AttnArgs {
   int32_t RB;    // query-row blocks per (b, k)
   int32_t RMAX;  // rows per row block (the last block may be partial)
   int32_t out_dtype;  // 0 f16, 1 bf16, 2 f32
-  int32_t W;          // launched workgroups
+  int32_t W;          // workers sharing the tiles (waves or workgroups, per kernel)
   float scale_log2;   // scale * log2(e)
-  float* part_o;      // [W + units, RMAX, H]
+  float* part_o;      // [W + units, RMAX, H], slot = worker + unit
   float* part_ml;     // [W + units, RMAX, 2]
   int32_t* counters;  // [units]
 };
@@ -173,7 +177,7 @@ __device__ __forceinline__ bool seq_valid(int32_t len, int32_t T, int32_t capaci
   return len >= T && len <= capacity;
 }
 
-// s_pre[0..B]: exclusive prefix sums of tiles per sequence (0 for invalid
+// s_pre[0..B]: exclusive prefix sums of steps per sequence (0 for invalid
 // lengths). Requires THREADS threads and a scratch of WAVES ints.
 __device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_wave) {
   const int tid = threadIdx.x;
@@ -184,7 +188,7 @@ __device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_
     int b = b0 + i;
     if (b < a.B) {
       int32_t len = a.seq_lens[b];
-      local += seq_valid(len, a.T, a.capacity) ? (len + TILE - 1) / TILE : 0;
+      local += seq_valid(len, a.T, a.capacity) ? (len + STEP - 1) / STEP : 0;
     }
   }
   // inclusive scan of `local` over the workgroup
@@ -205,43 +209,44 @@ __device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_
     if (b < a.B) {
       s_pre[b] = run;
       int32_t len = a.seq_lens[b];
-      run += seq_valid(len, a.T, a.capacity) ? (len + TILE - 1) / TILE : 0;
+      run += seq_valid(len, a.T, a.capacity) ? (len + STEP - 1) / STEP : 0;
     }
   }
   if (tid == THREADS - 1) s_pre[a.B] = carry + incl;
   __syncthreads();
 }
 
-// The workgroup's view of one unit segment.
+// A worker's view of one unit segment (a worker is one wave or one
+// workgroup, depending on the kernel).
 struct Segment {
   int b;          // sequence
   int k;          // key-value head
   int rb;         // query-row block
   int unit;       // (b * K + k) * RB + rb
   int seq_len;    // valid tokens
-  int t_begin;    // first tile of this segment (within the unit)
-  int t_end;      // one past the last tile
-  int n_parts;    // workgroups sharing the unit (1: this one writes the output directly)
-  int first_wg;   // first workgroup sharing the unit
+  int t_begin;    // first step of this segment (within the unit)
+  int t_end;      // one past the last step
+  int n_parts;    // workers sharing the unit (1: this one writes the output directly)
+  int first_wg;   // first worker sharing the unit
 };
 
 struct Partition {
-  int64_t total;  // tiles over all units
-  int w_eff;      // workgroups with work: min(W, total)
-  int64_t lo, hi; // this workgroup's flat tile range
+  int64_t total;  // steps over all units
+  int w_eff;      // workers with work: min(W, total); each then has >= 1 step
+  int64_t lo, hi; // this worker's flat step range
   int krb;        // K * RB
 
-  __device__ int owner(int64_t x) const {  // workgroup whose range holds tile x
+  __device__ int owner(int64_t x) const {  // worker whose range holds step x
     return (int)(((x + 1) * (int64_t)w_eff - 1) / total);
   }
 };
 
-__device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int32_t* s_pre) {
+__device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int32_t* s_pre,
+                                                    int w) {
   Partition p;
   p.krb = a.K * a.RB;
   p.total = (int64_t)s_pre[a.B] * p.krb;
   p.w_eff = (int)(p.total < (int64_t)a.W ? p.total : (int64_t)a.W);
-  const int w = blockIdx.x;
   if (w < p.w_eff) {
     p.lo = (int64_t)w * p.total / p.w_eff;
     p.hi = (int64_t)(w + 1) * p.total / p.w_eff;
@@ -251,7 +256,7 @@ __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int
   return p;
 }
 
-// Segment containing flat tile x (x < p.total).
+// Segment containing flat step x (x < p.total).
 __device__ __forceinline__ Segment find_segment(const AttnArgs& a, const int32_t* s_pre,
                                                 const Partition& p, int64_t x) {
   // first b with s_pre[b + 1] * krb > x
@@ -302,7 +307,7 @@ template <int H>
 __device__ void fill_invalid(const AttnArgs& a) {
   const float qnan = __int_as_float(0x7fc00000);
   const int units = a.B * a.K;
-  for (int u = blockIdx.x; u < units; u += a.W) {
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int b = u / a.K;
     if (seq_valid(a.seq_lens[b], a.T, a.capacity)) continue;
     const int k = u - b * a.K;
@@ -323,7 +328,7 @@ __device__ void fill_invalid(const AttnArgs& a) {
 // segment that met an out-of-range block-table entry: its partial is NaN.
 // Ends with a barrier, so LDS may be reused afterwards.
 template <int H, int NW>
-__device__ void finish_segment(const AttnArgs& a, const Segment& s, const float* s_m,
+__device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
                                const float* s_l, const float* s_o, bool bad, int32_t* s_flag) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const int row0 = s.rb * a.RMAX;
@@ -345,7 +350,7 @@ __device__ void finish_segment(const AttnArgs& a, const Segment& s, const float*
     __syncthreads();
     return;
   }
-  const int slot = blockIdx.x + s.unit;
+  const int slot = worker + s.unit;
   float* po = a.part_o + (int64_t)slot * a.RMAX * H;
   float* pml = a.part_ml + (int64_t)slot * a.RMAX * 2;
   for (int e = threadIdx.x; e < rows * H; e += THREADS) {
