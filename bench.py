@@ -50,7 +50,31 @@ def parse():
     p.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough to defeat the MALL)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only copy a MIB-mebibyte device buffer 10 times (known-size reference "
+                        "for the HBM byte counters) and print its bandwidth")
     return p.parse_args()
+
+
+def calibrate_copy(mib: int):
+    """Plain device-to-device copy of a known size: the reference that scales
+    FETCH_SIZE / WRITE_SIZE counters to bytes, and a copy-bandwidth figure."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                      "copy_GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 class Step:
@@ -90,6 +114,36 @@ class Step:
         f = self.kvc.decode if self.w.T == 1 else self.kvc.verify
         f(self.q, self.cache, self.seq_lens, self.max_len, out=self.out, out_dtype=self.w.dtype,
           num_workgroups=self.nwg, ws=self.ws)
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources (kv_cached_gqa_attention_amd/csrc)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "kv_cached_gqa_attention_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE) from the committed
+    rocprofv3 summary of this kernel and workload, or None when there is none
+    or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel.replace('_kernel', '')}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-json:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("source_hash") != source_hash():
+                    return None
+                return int(rec["fetch_bytes"] + rec["write_bytes"])
+    return None
 
 
 def kv_bytes(w, seq_lens) -> int:
@@ -150,6 +204,9 @@ def main():
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note only).", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     import torch
 
     from workloads import draw_prior_lengths, get_workload
@@ -189,21 +246,24 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # Attention kernel alone: HIP events on the stream the kernel runs on
-    # (torch's current stream is the one handed to the library).
+    # Attention kernel alone: back-to-back launches between two HIP events on
+    # the stream the kernel runs on (torch's current stream is the one handed
+    # to the library), so the average is the kernel's own duration.
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps * layers)]
-    for i in range(args.steps):
-        for l, s in enumerate(steps[i % reps]):
-            s.append()
-            a, b = ev[i * layers + l]
-            a.record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(reps):
+        for s in steps[i]:
             s.attend()
-            b.record(stream)
+    e0.record(stream)
+    for i in range(args.steps):
+        for s in steps[i % reps]:
+            s.attend()
+    e1.record(stream)
     torch.cuda.synchronize()
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    attn_ms = e0.elapsed_time(e1) / (args.steps * layers)
     achieved = step_bytes / (attn_ms * 1e-3) / 1e9
+    kernel = "attn_mfma_kernel" if w.G * w.T > (8 if w.H == 64 else 4) else "attn_valu_kernel"
+    traffic = profiled_traffic(kernel, w.name)
 
     value = step_bytes * layers / (ms_per_step * 1e-3) / 1e9
     tokens = w.B * w.T
@@ -238,13 +298,13 @@ def main():
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "attention_steps_per_s": round(1e3 / ms_per_step, 1),
         "roofline": {
-            "kernel": "attn_mfma_kernel" if w.G * w.T > 8 else "attn_valu_kernel",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "launch_ms": round(attn_ms, 5),
             "bytes_per_launch": step_bytes,
         },

@@ -35,10 +35,16 @@ __device__ __forceinline__ floatx4 mfma16(uint4 a, uint4 b, floatx4 c) {
   }
 }
 
+// 16-bit bits of a probability weight (finite, >= 0): round to nearest even
+// without the NaN path of the general conversion.
 template <bool BF>
 __device__ __forceinline__ uint32_t to16(float f) {
-  if constexpr (BF) return f32_to_bf16_bits(f);
-  else return f32_to_f16_bits(f);
+  if constexpr (BF) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  } else {
+    return f32_to_f16_bits(f);
+  }
 }
 template <bool BF>
 __device__ __forceinline__ float from16(uint32_t bits) {
@@ -55,29 +61,32 @@ __device__ __forceinline__ uint32_t swz_xor4(uint32_t x) {
 // octet: lane i holds x_i[0..7] (element 2w in the low half of word w), and
 // receives y_i[j] = x_j[i]. Block swaps of 4, 2, then 1 element(s).
 __device__ __forceinline__ uint4 transpose8(uint4 v, int i8) {
+  // Per-lane choices are selects, not branches (every lane runs both sides
+  // of a divergent branch anyway).
   uint32_t x0 = v.x, x1 = v.y, x2 = v.z, x3 = v.w;
   const bool b2 = (i8 & 4) != 0, b1 = (i8 & 2) != 0, b0 = (i8 & 1) != 0;
-  uint32_t s0 = b2 ? x0 : x2, s1 = b2 ? x1 : x3;
-  uint32_t r0 = swz_xor4(s0), r1 = swz_xor4(s1);
-  if (b2) { x0 = r0; x1 = r1; } else { x2 = r0; x3 = r1; }
-  s0 = b1 ? x0 : x1;
-  s1 = b1 ? x2 : x3;
-  r0 = dpp_u<DPP_QUAD_XOR2>(s0);
-  r1 = dpp_u<DPP_QUAD_XOR2>(s1);
-  if (b1) { x0 = r0; x2 = r1; } else { x1 = r0; x3 = r1; }
-  uint32_t p0 = dpp_u<DPP_QUAD_XOR1>(x0), p1 = dpp_u<DPP_QUAD_XOR1>(x1);
-  uint32_t p2 = dpp_u<DPP_QUAD_XOR1>(x2), p3 = dpp_u<DPP_QUAD_XOR1>(x3);
-  if (b0) {
-    x0 = (x0 & 0xffff0000u) | (p0 >> 16);
-    x1 = (x1 & 0xffff0000u) | (p1 >> 16);
-    x2 = (x2 & 0xffff0000u) | (p2 >> 16);
-    x3 = (x3 & 0xffff0000u) | (p3 >> 16);
-  } else {
-    x0 = (x0 & 0xffffu) | (p0 << 16);
-    x1 = (x1 & 0xffffu) | (p1 << 16);
-    x2 = (x2 & 0xffffu) | (p2 << 16);
-    x3 = (x3 & 0xffffu) | (p3 << 16);
-  }
+  uint32_t r0 = swz_xor4(b2 ? x0 : x2), r1 = swz_xor4(b2 ? x1 : x3);
+  x0 = b2 ? r0 : x0;
+  x1 = b2 ? r1 : x1;
+  x2 = b2 ? x2 : r0;
+  x3 = b2 ? x3 : r1;
+  r0 = dpp_u<DPP_QUAD_XOR2>(b1 ? x0 : x1);
+  r1 = dpp_u<DPP_QUAD_XOR2>(b1 ? x2 : x3);
+  x0 = b1 ? r0 : x0;
+  x2 = b1 ? r1 : x2;
+  x1 = b1 ? x1 : r0;
+  x3 = b1 ? x3 : r1;
+  const uint32_t p0 = dpp_u<DPP_QUAD_XOR1>(x0), p1 = dpp_u<DPP_QUAD_XOR1>(x1);
+  const uint32_t p2 = dpp_u<DPP_QUAD_XOR1>(x2), p3 = dpp_u<DPP_QUAD_XOR1>(x3);
+  // v_perm_b32(S0 = own word, S1 = partner's word): bytes 0-3 index S1,
+  // 4-7 index S0. Odd lanes keep their high half and take the partner's
+  // high half as low half ([p2 p3 x2 x3]); even lanes keep their low half
+  // and take the partner's low half as high half ([x0 x1 p0 p1]).
+  const uint32_t sel = b0 ? 0x07060302u : 0x01000504u;
+  x0 = __builtin_amdgcn_perm(x0, p0, sel);
+  x1 = __builtin_amdgcn_perm(x1, p1, sel);
+  x2 = __builtin_amdgcn_perm(x2, p2, sel);
+  x3 = __builtin_amdgcn_perm(x3, p3, sel);
   return make_uint4(x0, x1, x2, x3);
 }
 
@@ -219,8 +228,8 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
           for (int i = 0; i < 4; ++i) mt = fmaxf(mt, p[mb][i]);
         mt = fmaxf(mt, shfl_xor_f(mt, 16));
         mt = fmaxf(mt, shfl_xor_f(mt, 32));
-        const float mn = fmaxf(m[nb], mt);
-        if (mn > m[nb]) {
+        if (__builtin_amdgcn_ballot_w64(mt > m[nb] + RESCALE_MARGIN) != 0ull) {
+          const float mn = mt > m[nb] + RESCALE_MARGIN ? mt : m[nb];
           const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);
           l[nb] *= alpha;
 #pragma unroll

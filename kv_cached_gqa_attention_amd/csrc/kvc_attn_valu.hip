@@ -178,6 +178,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
       }
 
       // ---- online softmax; the rescale runs only when some row's max grew
+      // past the margin
       float mn[R];
       bool grew = false;
 #pragma unroll
@@ -185,8 +186,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
         float mt = sc[r][0];
 #pragma unroll
         for (int i = 1; i < RPG; ++i) mt = fmaxf(mt, sc[r][i]);
-        mn[r] = fmaxf(m[r], mt);
-        grew |= mn[r] > m[r];
+        const bool up = mt > m[r] + RESCALE_MARGIN;
+        mn[r] = up ? mt : m[r];
+        grew |= up;
       }
       if (__builtin_amdgcn_ballot_w64(grew) != 0ull) {
 #pragma unroll

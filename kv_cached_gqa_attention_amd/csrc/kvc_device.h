@@ -33,6 +33,11 @@ constexpr int THREADS = 64 * WAVES;
 constexpr int STEP = TILE * WAVES;  // tokens per partition step (one tile per wave)
 constexpr float NEG_BIG = -1.0e30f;  // running max before any visible key; exp2(NEG_BIG - x) == 0
 constexpr float LN2 = 0.69314718055994531f;
+// The running max is raised only when a tile's max exceeds it by more than
+// this (log2 units): weights exp2(s - m) then stay <= 2^8 and accumulators
+// stay far inside fp32 range, and most tiles skip the rescale. The result is
+// the same function: m is only the reference point of l and o.
+constexpr float RESCALE_MARGIN = 8.0f;
 
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf162_t;
