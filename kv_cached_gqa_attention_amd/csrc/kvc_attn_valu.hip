@@ -96,6 +96,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
 
   // This wave's tile of the first step, all K rows then all V rows (the
   // loop's issue order).
+  // A unit's query rows, this lane's dims. The next unit's rows are loaded
+  // into the same registers right after the last q.k of the current unit,
+  // so they arrive while the workgroup publishes the current one.
+  uint4 qreg[R][NCH];
+  auto load_q = [&](const Segment& g) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const char* qrow = a.q + row_index(a, g.b, g.k, r) * (H * 2);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) qreg[r][c] = load16(qrow + c * SLICE * 2 + li * 16);
+    }
+  };
+  load_q(cur);
   bool bad_cur = false, bad_nxt = false;
   uint4 kr[RPG][NCH], vr[RPG][NCH];
   load_rows(kbase(cur), cur, cur.t_begin * WAVES + wave, kr, bad_cur);
@@ -118,16 +131,6 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
       for (int d = 0; d < DPL; ++d) o[r][d] = 0.f;
     }
-    // The unit's query rows, this lane's dims (the unit's first K/V tile is
-    // already in flight, so this load adds little latency).
-    uint4 qreg[R][NCH];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const char* qrow = a.q + row_index(a, cur.b, cur.k, r) * (H * 2);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) qreg[r][c] = load16(qrow + c * SLICE * 2 + li * 16);
-    }
-
     for (int st = cur.t_begin; st < cur.t_end; ++st) {
       const int ti = st * WAVES + wave;  // this wave's tile of step st
       // ---- scores (base 2)
@@ -232,6 +235,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
       load_rows(nvb, ng, tn, vr, nbad);
       if (hop) bad_nxt |= nbad; else bad_cur |= nbad;
     }
+    if (has_next) load_q(nxt);
 
     // ---- combine this wave's lane groups, park the wave's state in LDS
 #pragma unroll

@@ -389,24 +389,45 @@ __device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, 
   __syncthreads();
   if (s_flag[0]) {
     // Every other partial of the unit was acknowledged before its counter
-    // increment, which preceded ours; device-coherent loads see them.
+    // increment, which preceded ours; device-coherent loads see them. The
+    // partials are folded in chunks of 8 whose loads are issued together
+    // (one memory round trip per chunk), with an online rescale between
+    // chunks.
+    constexpr int CH = 8;
+    const int n = s.n_parts;
+#pragma unroll 2
     for (int e = threadIdx.x; e < rows * H; e += THREADS) {
       const int r = e / H, h = e - (e / H) * H;
-      float M = NEG_BIG;
-      for (int i = 0; i < s.n_parts; ++i) {
-        const float* ml = a.part_ml + (int64_t)(s.first_wg + i + s.unit) * a.RMAX * 2;
-        M = fmaxf(M, load_coherent(ml + r * 2));
-      }
-      float L = 0.f, O = 0.f;
-      for (int i = 0; i < s.n_parts; ++i) {
-        const int64_t sl = s.first_wg + i + s.unit;
-        const float* ml = a.part_ml + sl * a.RMAX * 2;
-        const float mi = load_coherent(ml + r * 2);
-        const float li = load_coherent(ml + r * 2 + 1);
-        const float oi = load_coherent(a.part_o + (sl * a.RMAX + r) * H + h);
-        const float sc = exp2f(mi - M);
-        L += sc * li;
-        O += sc * oi;
+      float M = NEG_BIG, L = 0.f, O = 0.f;
+      for (int base = 0; base < n; base += CH) {
+        float mi[CH], li[CH], oi[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const bool ok = base + j < n;
+          const int64_t sl = ok ? (int64_t)s.first_wg + base + j + s.unit : (int64_t)s.first_wg + s.unit;
+          const float* ml = a.part_ml + sl * a.RMAX * 2 + r * 2;
+          mi[j] = load_coherent(ml);
+          li[j] = load_coherent(ml + 1);
+          oi[j] = load_coherent(a.part_o + (sl * a.RMAX + r) * H + h);
+          if (!ok) {
+            mi[j] = NEG_BIG;
+            li[j] = 0.f;
+            oi[j] = 0.f;
+          }
+        }
+        float Mc = M;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) Mc = fmaxf(Mc, mi[j]);
+        const float keep = exp2f(M - Mc);
+        L *= keep;
+        O *= keep;
+        M = Mc;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const float w = exp2f(mi[j] - M);
+          L += w * li[j];
+          O += w * oi[j];
+        }
       }
       write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
     }
