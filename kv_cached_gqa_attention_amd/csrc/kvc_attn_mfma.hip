@@ -96,10 +96,10 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = H / 32;     // k-steps of S^T over h
   constexpr int MH = H / 16;     // 16-row h blocks of O^T
 
-  extern __shared__ int32_t s_pre[];  // [B + 1]
+  extern __shared__ int32_t s_pre[];  // [2B + 1]
   __shared__ float s_m[RMAX], s_l[RMAX];
   __shared__ float s_o[RMAX * H];
-  __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[1];
+  __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[2];
 
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a);
@@ -114,6 +114,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
   // token of k-slot (g, j): j < 4 -> 4g + j ; j >= 4 -> 16 + 4g + (j - 4)
   const int vtok = (i8 < 4) ? (4 * g + i8) : (16 + 4 * g + i8 - 4);
 
+  SharedUnits shared;
   for (int64_t x = part.lo; x < part.hi;) {
     const Segment s = find_segment(a, s_pre, part, x);
     x += s.t_end - s.t_begin;
@@ -309,15 +310,16 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    finish_segment<H, 1>(a, s, blockIdx.x, s_m, s_l, s_o, segbad, s_flag);
+    finish_segment<H, 1>(a, s, blockIdx.x, s_m, s_l, s_o, segbad, shared);
   }
+  count_and_merge<H>(a, shared, s_flag);
 }
 
 // ---------------------------------------------------------------- launch
 
 template <bool BF, int H, int NB, bool PAGED>
 static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
-  const size_t shmem = (size_t)(a.B + 1) * sizeof(int32_t);
+  const size_t shmem = (size_t)(2 * a.B + 1) * sizeof(int32_t);
   // one worker per workgroup
   hipLaunchKernelGGL((attn_mfma_kernel<BF, H, NB, PAGED>), dim3(a.W), dim3(THREADS), shmem, stream, a);
   return hipGetLastError();

@@ -44,10 +44,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
   constexpr int SLICE = H / NCH;       // elements covered by one chunk across the group
   static_assert(DPL == 8 || DPL == 16, "8 or 16 dims per lane");
 
-  extern __shared__ int32_t s_pre[];   // [B + 1]
+  extern __shared__ int32_t s_pre[];   // [2B + 1]
   __shared__ float s_m[WAVES * R], s_l[WAVES * R];
   __shared__ float s_o[WAVES * R * H];
-  __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[1];
+  __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[2];
 
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a);
@@ -94,11 +94,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
   Segment cur = find_segment(a, s_pre, part, part.lo);
   int64_t x_next = part.lo + (cur.t_end - cur.t_begin);
 
-  // This wave's tile of the first step, all K rows then all V rows (the
-  // loop's issue order).
-  // A unit's query rows, this lane's dims. The next unit's rows are loaded
-  // into the same registers right after the last q.k of the current unit,
-  // so they arrive while the workgroup publishes the current one.
+  // A unit's query rows, this lane's dims. They are loaded again with every
+  // K prefetch (the rows of the unit the prefetched tile belongs to; they
+  // stay in L1), so the query loads are never newer than the tile loads and
+  // waiting for them never waits for a tile prefetch. At a unit switch this
+  // brings in the next unit's rows during the publish of the current one.
   uint4 qreg[R][NCH];
   auto load_q = [&](const Segment& g) {
 #pragma unroll
@@ -116,6 +116,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
   load_rows(vbase(cur), cur, cur.t_begin * WAVES + wave, vr, bad_cur);
   __builtin_amdgcn_sched_barrier(0);
 
+  SharedUnits shared;
   while (true) {
     const bool has_next = x_next < part.hi;
     const Segment nxt = has_next ? find_segment(a, s_pre, part, x_next) : cur;
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
       const char* nkb = hop ? kbase(nxt) : kbase(cur);
       const char* nvb = hop ? vbase(nxt) : vbase(cur);
       bool nbad = false;
+      load_q(ng);
       load_rows(nkb, ng, tn, kr, nbad);
 #pragma unroll
       for (int i = 0; i < RPG; ++i)
@@ -235,7 +237,6 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
       load_rows(nvb, ng, tn, vr, nbad);
       if (hop) bad_nxt |= nbad; else bad_cur |= nbad;
     }
-    if (has_next) load_q(nxt);
 
     // ---- combine this wave's lane groups, park the wave's state in LDS
 #pragma unroll
@@ -275,8 +276,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
     // The next unit's first tiles are in flight while the workgroup combines
-    // and publishes this one.
-    finish_segment<H, WAVES>(a, cur, blockIdx.x, s_m, s_l, s_o, segbad, s_flag);
+    // and writes this one.
+    finish_segment<H, WAVES>(a, cur, blockIdx.x, s_m, s_l, s_o, segbad, shared);
 
     if (!has_next) break;
     cur = nxt;
@@ -284,6 +285,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
     bad_cur = bad_nxt;
     bad_nxt = false;
   }
+  count_and_merge<H>(a, shared, s_flag);
 }
 
 // ---------------------------------------------------------------- launch
@@ -295,7 +297,7 @@ static hipError_t launch_valu_t(const AttnArgs& a, hipStream_t stream) {
   // (a few spills outside the loop are cheap); otherwise let the compiler
   // take the registers it wants.
   constexpr int WPE = (H == 128 && R <= 4) || (H == 64 && R <= 6) ? 2 : 1;
-  const size_t shmem = (size_t)(a.B + 1) * sizeof(int32_t);
+  const size_t shmem = (size_t)(2 * a.B + 1) * sizeof(int32_t);
   // one worker per workgroup; its waves interleave the tiles
   hipLaunchKernelGGL((attn_valu_kernel<BF, H, R, LPR, PAGED, WPE>), dim3(a.W), dim3(THREADS),
                      shmem, stream, a);

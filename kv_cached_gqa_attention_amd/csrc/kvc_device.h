@@ -183,7 +183,11 @@ __device__ __forceinline__ bool seq_valid(int32_t len, int32_t T, int32_t capaci
 }
 
 // s_pre[0..B]: exclusive prefix sums of steps per sequence (0 for invalid
-// lengths). Requires THREADS threads and a scratch of WAVES ints.
+// lengths); s_pre[B + 1 + b]: the length of sequence b, so that later reads
+// of it are LDS reads rather than global loads (a global load inside the
+// unit loop would be waited for together with the tile prefetches).
+// s_pre holds 2B + 1 ints. Requires THREADS threads and a scratch of WAVES
+// ints.
 __device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_wave) {
   const int tid = threadIdx.x;
   const int per = (a.B + THREADS - 1) / THREADS;
@@ -214,6 +218,7 @@ __device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_
     if (b < a.B) {
       s_pre[b] = run;
       int32_t len = a.seq_lens[b];
+      s_pre[a.B + 1 + b] = len;
       run += seq_valid(len, a.T, a.capacity) ? (len + STEP - 1) / STEP : 0;
     }
   }
@@ -250,7 +255,7 @@ __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int
                                                     int w) {
   Partition p;
   p.krb = a.K * a.RB;
-  p.total = (int64_t)s_pre[a.B] * p.krb;
+  p.total = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[a.B]) * p.krb;
   p.w_eff = (int)(p.total < (int64_t)a.W ? p.total : (int64_t)a.W);
   if (w < p.w_eff) {
     p.lo = (int64_t)w * p.total / p.w_eff;
@@ -270,17 +275,19 @@ __device__ __forceinline__ Segment find_segment(const AttnArgs& a, const int32_t
     int mid = (lo + hi) >> 1;
     if ((int64_t)s_pre[mid + 1] * p.krb > x) hi = mid; else lo = mid + 1;
   }
+  // every field is wave-uniform; readfirstlane keeps them in scalar registers
   Segment s;
-  s.b = lo;
-  const int64_t base = (int64_t)s_pre[lo] * p.krb;
-  const int tb = s_pre[lo + 1] - s_pre[lo];
-  const int64_t off = x - base;
-  const int ur = (int)(off / tb);
+  s.b = __builtin_amdgcn_readfirstlane(lo);
+  const int p0 = __builtin_amdgcn_readfirstlane(s_pre[s.b]);
+  const int tb = __builtin_amdgcn_readfirstlane(s_pre[s.b + 1]) - p0;
+  const int64_t base = (int64_t)p0 * p.krb;
+  const int off = (int)(x - base);  // < tb * krb
+  const int ur = off / tb;
   s.k = ur / a.RB;
   s.rb = ur - s.k * a.RB;
   s.unit = (s.b * a.K + s.k) * a.RB + s.rb;
-  s.seq_len = a.seq_lens[s.b];
-  s.t_begin = (int)(off - (int64_t)ur * tb);
+  s.seq_len = __builtin_amdgcn_readfirstlane(s_pre[a.B + 1 + s.b]);
+  s.t_begin = off - ur * tb;
   const int64_t room = p.hi - x;
   s.t_end = (int64_t)(tb - s.t_begin) < room ? tb : s.t_begin + (int)room;
   const int64_t ustart = x - s.t_begin;
@@ -325,49 +332,67 @@ __device__ void fill_invalid(const AttnArgs& a) {
   }
 }
 
-// Finish one unit segment whose per-wave states sit in LDS:
+// Finishing one unit segment whose per-wave states sit in LDS:
 //   s_m[w * RMAX + r], s_l[w * RMAX + r], s_o[(w * RMAX + r) * H + h]
-// for NW wave states. Combines the waves, then either writes the output (the
-// segment is the whole unit) or writes a partial and, if this workgroup is
-// the last of the unit, merges all of the unit's partials. `bad` marks a
-// segment that met an out-of-range block-table entry: its partial is NaN.
-// Ends with a barrier, so LDS may be reused afterwards.
+// for NW wave states. The waves' states are combined, then either the output
+// is written (the segment is the whole unit: finish_direct) or a partial is
+// stored (store_partial). A worker's shared units are counted together once
+// its whole range is done (count_and_merge): the workgroup that counts a
+// unit's last partial merges them all (merge_partials). Waiting for the
+// partial stores and for the count's return only once per worker, at its
+// end, keeps both latencies out of the middle of the range. `bad` marks a
+// segment that met an out-of-range block-table entry: its result is NaN.
+
+// Combined state of the NW waves for (row r, dim h).
 template <int H, int NW>
-__device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
-                               const float* s_l, const float* s_o, bool bad, int32_t* s_flag) {
+__device__ __forceinline__ void combine_waves(const AttnArgs& a, const float* s_m, const float* s_l,
+                                              const float* s_o, int r, int h, float& M, float& L,
+                                              float& O) {
+  M = NEG_BIG;
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * a.RMAX + r]);
+  L = 0.f;
+  O = 0.f;
+  for (int w = 0; w < NW; ++w) {
+    const float sc = exp2f(s_m[w * a.RMAX + r] - M);
+    L += sc * s_l[w * a.RMAX + r];
+    O += sc * s_o[(w * a.RMAX + r) * H + h];
+  }
+}
+
+// The segment is its whole unit: write the output. Ends with a barrier, so
+// LDS may be reused afterwards.
+template <int H, int NW>
+__device__ void finish_direct(const AttnArgs& a, const Segment& s, const float* s_m,
+                              const float* s_l, const float* s_o, bool bad) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const int row0 = s.rb * a.RMAX;
   const float qnan = __int_as_float(0x7fc00000);
-  if (s.n_parts == 1) {
-    for (int e = threadIdx.x; e < rows * H; e += THREADS) {
-      const int r = e / H, h = e - (e / H) * H;
-      float M = NEG_BIG;
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * a.RMAX + r]);
-      float L = 0.f, O = 0.f;
-      for (int w = 0; w < NW; ++w) {
-        const float sc = exp2f(s_m[w * a.RMAX + r] - M);
-        L += sc * s_l[w * a.RMAX + r];
-        O += sc * s_o[(w * a.RMAX + r) * H + h];
-      }
-      if (bad) O = L = M = qnan;
-      write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
-    }
-    __syncthreads();
-    return;
+  for (int e = threadIdx.x; e < rows * H; e += THREADS) {
+    const int r = e / H, h = e - (e / H) * H;
+    float M, L, O;
+    combine_waves<H, NW>(a, s_m, s_l, s_o, r, h, M, L, O);
+    if (bad) O = L = M = qnan;
+    write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
   }
+  __syncthreads();
+}
+
+// Store this worker's partial of the unit. The stores are device-coherent
+// (they bypass this XCD's L2 copy); they are waited for in count_and_merge,
+// before the partial is counted. Ends with a barrier, so LDS may be reused
+// afterwards.
+template <int H, int NW>
+__device__ void store_partial(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
+                              const float* s_l, const float* s_o, bool bad) {
+  const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
+  const float qnan = __int_as_float(0x7fc00000);
   const int slot = worker + s.unit;
   float* po = a.part_o + (int64_t)slot * a.RMAX * H;
   float* pml = a.part_ml + (int64_t)slot * a.RMAX * 2;
   for (int e = threadIdx.x; e < rows * H; e += THREADS) {
     const int r = e / H, h = e - (e / H) * H;
-    float M = NEG_BIG;
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * a.RMAX + r]);
-    float L = 0.f, O = 0.f;
-    for (int w = 0; w < NW; ++w) {
-      const float sc = exp2f(s_m[w * a.RMAX + r] - M);
-      L += sc * s_l[w * a.RMAX + r];
-      O += sc * s_o[(w * a.RMAX + r) * H + h];
-    }
+    float M, L, O;
+    combine_waves<H, NW>(a, s_m, s_l, s_o, r, h, M, L, O);
     if (bad) O = L = M = qnan;
     store_coherent(po + r * H + h, O);
     if (h == 0) {
@@ -375,66 +400,111 @@ __device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, 
       store_coherent(pml + r * 2 + 1, L);
     }
   }
-  // Publish the partial, then count it. The partial's stores are device-
-  // coherent (they bypass this XCD's L2 copy), so waiting for their
-  // acknowledgement before the barrier is the whole release: no L2-wide
-  // write-back or invalidate is needed.
+  __syncthreads();
+}
+
+// Count a stored partial (one thread, after its stores were acknowledged);
+// true for the unit's last one.
+__device__ __forceinline__ bool count_partial(const AttnArgs& a, const Segment& s) {
+  const int prev = __hip_atomic_fetch_add(&a.counters[s.unit], 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+  return prev == s.n_parts - 1;
+}
+
+// Merge all partials of the unit and write the output; called by the
+// workgroup that counted the last one. Every other partial was acknowledged
+// before its count, which preceded ours; device-coherent loads see them. The
+// partials are folded in chunks of 8 whose loads are issued together (one
+// memory round trip per chunk), with an online rescale between chunks. The
+// count is reset for the next call.
+template <int H>
+__device__ void merge_partials(const AttnArgs& a, const Segment& s) {
+  const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
+  const int row0 = s.rb * a.RMAX;
+  constexpr int CH = 8;
+  const int n = s.n_parts;
+#pragma unroll 2
+  for (int e = threadIdx.x; e < rows * H; e += THREADS) {
+    const int r = e / H, h = e - (e / H) * H;
+    float M = NEG_BIG, L = 0.f, O = 0.f;
+    for (int base = 0; base < n; base += CH) {
+      float mi[CH], li[CH], oi[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const bool ok = base + j < n;
+        const int64_t sl = ok ? (int64_t)s.first_wg + base + j + s.unit : (int64_t)s.first_wg + s.unit;
+        const float* ml = a.part_ml + sl * a.RMAX * 2 + r * 2;
+        mi[j] = load_coherent(ml);
+        li[j] = load_coherent(ml + 1);
+        oi[j] = load_coherent(a.part_o + (sl * a.RMAX + r) * H + h);
+        if (!ok) {
+          mi[j] = NEG_BIG;
+          li[j] = 0.f;
+          oi[j] = 0.f;
+        }
+      }
+      float Mc = M;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) Mc = fmaxf(Mc, mi[j]);
+      const float keep = exp2f(M - Mc);
+      L *= keep;
+      O *= keep;
+      M = Mc;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const float w = exp2f(mi[j] - M);
+        L += w * li[j];
+        O += w * oi[j];
+      }
+    }
+    write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&a.counters[s.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The units of a worker's range that it shares with other workers: only the
+// first and the last segment of a range can be part of a shared unit (every
+// segment in between is a whole unit).
+struct SharedUnits {
+  Segment s0, s1;
+  int n = 0;
+  __device__ void add(const Segment& s) {
+    if (n == 0) s0 = s; else s1 = s;
+    ++n;
+  }
+};
+
+// Finish a segment: the output, or a partial to be counted at the worker's
+// end. Ends with a barrier, so LDS may be reused afterwards.
+template <int H, int NW>
+__device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
+                               const float* s_l, const float* s_o, bool bad, SharedUnits& sh) {
+  if (s.n_parts == 1) {
+    finish_direct<H, NW>(a, s, s_m, s_l, s_o, bad);
+  } else {
+    store_partial<H, NW>(a, s, worker, s_m, s_l, s_o, bad);
+    sh.add(s);
+  }
+}
+
+// At the end of a worker's range: once its partial stores are acknowledged,
+// count them, then merge every unit whose last partial this worker counted.
+// Needs s_flag[2] in LDS.
+template <int H>
+__device__ void count_and_merge(const AttnArgs& a, const SharedUnits& sh, int32_t* s_flag) {
+  if (sh.n == 0) return;
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(&a.counters[s.unit], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    s_flag[0] = (prev == s.n_parts - 1);
+    const bool f0 = count_partial(a, sh.s0);
+    const bool f1 = sh.n > 1 && count_partial(a, sh.s1);
+    s_flag[0] = f0;
+    s_flag[1] = f1;
   }
   __syncthreads();
-  if (s_flag[0]) {
-    // Every other partial of the unit was acknowledged before its counter
-    // increment, which preceded ours; device-coherent loads see them. The
-    // partials are folded in chunks of 8 whose loads are issued together
-    // (one memory round trip per chunk), with an online rescale between
-    // chunks.
-    constexpr int CH = 8;
-    const int n = s.n_parts;
-#pragma unroll 2
-    for (int e = threadIdx.x; e < rows * H; e += THREADS) {
-      const int r = e / H, h = e - (e / H) * H;
-      float M = NEG_BIG, L = 0.f, O = 0.f;
-      for (int base = 0; base < n; base += CH) {
-        float mi[CH], li[CH], oi[CH];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          const bool ok = base + j < n;
-          const int64_t sl = ok ? (int64_t)s.first_wg + base + j + s.unit : (int64_t)s.first_wg + s.unit;
-          const float* ml = a.part_ml + sl * a.RMAX * 2 + r * 2;
-          mi[j] = load_coherent(ml);
-          li[j] = load_coherent(ml + 1);
-          oi[j] = load_coherent(a.part_o + (sl * a.RMAX + r) * H + h);
-          if (!ok) {
-            mi[j] = NEG_BIG;
-            li[j] = 0.f;
-            oi[j] = 0.f;
-          }
-        }
-        float Mc = M;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) Mc = fmaxf(Mc, mi[j]);
-        const float keep = exp2f(M - Mc);
-        L *= keep;
-        O *= keep;
-        M = Mc;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          const float w = exp2f(mi[j] - M);
-          L += w * li[j];
-          O += w * oi[j];
-        }
-      }
-      write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
-    }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&a.counters[s.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
+  if (s_flag[0]) merge_partials<H>(a, sh.s0);
+  if (s_flag[1]) merge_partials<H>(a, sh.s1);
 }
 
 }  // namespace kvc
