@@ -50,6 +50,10 @@ def parse():
     p.add_argument("--replicas", type=int, default=0, help="cache replicas (0 = enough to defeat the MALL)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--mode", choices=("fused", "separate"), default="fused",
+                   help="fused: one append_attend call per layer; separate: append, then attend")
+    p.add_argument("--graph", action="store_true",
+                   help="capture each replica's step in a HIP graph and replay it (launch-bound shapes)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only copy a MIB-mebibyte device buffer 10 times (known-size reference "
                         "for the HBM byte counters) and print its bandwidth")
@@ -109,6 +113,11 @@ class Step:
 
     def append(self):
         self.kvc.append(self.cache, self.inp.k_new, self.inp.v_new, self.seq_lens)
+
+    def append_attend(self):
+        self.kvc.append_attend(self.q, self.inp.k_new, self.inp.v_new, self.cache, self.seq_lens,
+                               self.max_len, out=self.out, out_dtype=self.w.dtype,
+                               num_workgroups=self.nwg, ws=self.ws)
 
     def attend(self):
         f = self.kvc.decode if self.w.T == 1 else self.kvc.verify
@@ -231,10 +240,35 @@ def main():
              for r in range(reps)]
     torch.cuda.synchronize()
 
-    def run_step(i):
+    def eager_step(i):
         for s in steps[i % reps]:
-            s.append()
-            s.attend()
+            if args.mode == "fused":
+                s.append_attend()
+            else:
+                s.append()
+                s.attend()
+
+    # The step is the same work either way; with --graph each replica's step
+    # is captured once (after an eager warm-up) and replayed.
+    graphs = None
+    if args.graph:
+        for i in range(reps):
+            eager_step(i)
+        torch.cuda.synchronize()
+        graphs = []
+        side = torch.cuda.Stream(dev)
+        for i in range(reps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                eager_step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(i):
+        if graphs is not None:
+            graphs[i % reps].replay()
+        else:
+            eager_step(i)
 
     for i in range(args.warmup):
         run_step(i)
@@ -251,13 +285,16 @@ def main():
     # to the library), so the average is the kernel's own duration.
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the dominant kernel: the fused call's attention kernel (its appends
+    # rewrite the same rows), or the attention kernel of the separate form
+    one = (lambda s: s.append_attend()) if args.mode == "fused" else (lambda s: s.attend())
     for i in range(reps):
         for s in steps[i]:
-            s.attend()
+            one(s)
     e0.record(stream)
     for i in range(args.steps):
         for s in steps[i % reps]:
-            s.attend()
+            one(s)
     e1.record(stream)
     torch.cuda.synchronize()
     attn_ms = e0.elapsed_time(e1) / (args.steps * layers)
@@ -292,6 +329,7 @@ def main():
             "kv_bytes_per_step": step_bytes * layers,
             "mean_seq_len": float(np.mean(seq_lens)),
             "replicas": reps,
+            "mode": args.mode + (" + graph" if args.graph else ""),
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

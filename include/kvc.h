@@ -175,6 +175,29 @@ kvc_status kvc_attn_verify(const kvc_cache *cache, const void *q, void *out, int
                            size_t workspace_bytes, void *stream);
 
 /*
+ * Append and attend in one call: the effect of kvc_append(cache, k_new,
+ * v_new, B, T, K, H, seq_lens, stream) followed by kvc_attn_verify (T >= 1;
+ * T = 1 is decode) with the same arguments, on the same stream. The new rows
+ * are written into the cache as by kvc_append, and the attention sees them
+ * ("Making inference cheap: KV cache, batching and quantization": each step
+ * extends the cache by the new token's rows and attends over the whole
+ * cache). It saves the separate append launch: when every (b, k) is served
+ * by one row block (G * T <= 64, true for all decode and short verify
+ * shapes) the append happens inside the attention kernel, each new row
+ * written by the workgroup that later reads it; otherwise the call enqueues
+ * the append kernel and then the attention kernel.
+ * k_new, v_new: [B, T, K, H] in cache->dtype, 16-byte aligned (not modified).
+ * Workspace as kvc_attn_verify, same size. Errors: as kvc_append and
+ * kvc_attn_verify together. Outputs for sequences with an invalid length are
+ * NaN and their rows are not appended, as with the two separate calls.
+ */
+kvc_status kvc_append_attend(const kvc_cache *cache, const void *k_new, const void *v_new,
+                             const void *q, void *out, int out_dtype, float *lse, int B, int T,
+                             int N, int K, int H, const int32_t *seq_lens, int max_seq_len,
+                             float scale, int num_workgroups, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
  * Host query: workspace bytes needed by kvc_attn_decode (T = 1) or
  * kvc_attn_verify with the same B, T, N, K, H, max_seq_len and
  * num_workgroups. Returns 0 for invalid shapes. Uses the current device's

@@ -2,7 +2,7 @@
 
 The product is the C-ABI library ``libkvc.so`` (``include/kvc.h``): append of
 new K/V rows, split-KV decode and causal verify attention over contiguous or
-block-paged caches, in hand-written HIP kernels. This package is its Python
+block-paged caches, and both fused in one call, in hand-written HIP kernels. This package is its Python
 binding; PyTorch supplies device memory and streams.
 """
 
@@ -10,6 +10,7 @@ from .api import (
     Cache,
     KvcError,
     append,
+    append_attend,
     decode,
     gather,
     status_string,
@@ -22,6 +23,7 @@ __all__ = [
     "Cache",
     "KvcError",
     "append",
+    "append_attend",
     "decode",
     "gather",
     "status_string",

@@ -27,6 +27,7 @@ EXPORTS = (
     "kvc_append",
     "kvc_attn_decode",
     "kvc_attn_verify",
+    "kvc_append_attend",
     "kvc_workspace_bytes",
     "kvc_status_string",
     "kvc_gather",
@@ -77,6 +78,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvc_attn_verify.argtypes = [cache_p, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
                                     vp, c_int, c_float, c_int, vp, c_size_t, vp]
     lib.kvc_attn_verify.restype = c_int
+    lib.kvc_append_attend.argtypes = [cache_p, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int,
+                                      c_int, c_int, vp, c_int, ctypes.c_float, c_int, vp, c_size_t,
+                                      vp]
+    lib.kvc_append_attend.restype = c_int
     lib.kvc_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int]
     lib.kvc_workspace_bytes.restype = c_size_t
     lib.kvc_status_string.argtypes = [c_int]

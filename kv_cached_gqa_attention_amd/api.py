@@ -136,6 +136,15 @@ def workspace(device, nbytes: int) -> torch.Tensor:
 
 def append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, seq_lens: torch.Tensor):
     """Write ``k_new``/``v_new`` [B, T, K, H] at positions seq_lens[b] - T + t."""
+    _check_new_rows(cache, k_new, v_new, seq_lens)
+    B, T, K, H = k_new.shape
+    desc = cache.descriptor()
+    st = _lib.load().kvc_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), B, T, K, H,
+                                _ptr(seq_lens), _stream(k_new.device))
+    _check(st, "kvc_append")
+
+
+def _check_new_rows(cache, k_new, v_new, seq_lens):
     _gpu(k_new, "k_new")
     _gpu(v_new, "v_new")
     _gpu(seq_lens, "seq_lens")
@@ -147,14 +156,10 @@ def append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, seq_lens: tor
         raise ValueError("new rows must have the cache dtype")
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
-    B, T, K, H = k_new.shape
-    desc = cache.descriptor()
-    st = _lib.load().kvc_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), B, T, K, H,
-                                _ptr(seq_lens), _stream(k_new.device))
-    _check(st, "kvc_append")
 
 
-def _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, return_lse, out, ws, T):
+def _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, return_lse, out, ws, T,
+          new_rows=None):
     _gpu(q, "q")
     _gpu(seq_lens, "seq_lens")
     if not q.is_contiguous():
@@ -180,7 +185,12 @@ def _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, ret
     lib = _lib.load()
     common = (_ptr(seq_lens), int(max_seq_len), float(scale), int(num_workgroups), _ptr(ws),
               ws.numel() * ws.element_size(), _stream(q.device))
-    if T == 1 and q.dim() == 3:
+    if new_rows is not None:
+        k_new, v_new = new_rows
+        st = lib.kvc_append_attend(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                   _DT[out_dtype], _ptr(lse), B, T, N, K, H, *common)
+        where = "kvc_append_attend"
+    elif T == 1 and q.dim() == 3:
         st = lib.kvc_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(out), _DT[out_dtype], _ptr(lse),
                                  B, N, K, H, *common)
         where = "kvc_attn_decode"
@@ -208,6 +218,22 @@ def verify(q, cache: Cache, seq_lens, max_seq_len, scale=None, out_dtype=None, n
         raise ValueError("verify takes q [B, T, N, H]")
     return _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, return_lse, out,
                  ws, q.shape[1])
+
+
+def append_attend(q, k_new, v_new, cache: Cache, seq_lens, max_seq_len, scale=None, out_dtype=None,
+                  num_workgroups=0, return_lse=False, out=None, ws=None):
+    """``append`` then ``decode`` (q [B, N, H]) or ``verify`` (q [B, T, N, H]) in one call.
+
+    k_new, v_new: [B, T, K, H]. Same results as the two calls.
+    """
+    if q.dim() not in (3, 4):
+        raise ValueError("append_attend takes q [B, N, H] or [B, T, N, H]")
+    _check_new_rows(cache, k_new, v_new, seq_lens)
+    T = 1 if q.dim() == 3 else q.shape[1]
+    if k_new.shape[0] != q.shape[0] or k_new.shape[1] != T:
+        raise ValueError("k_new must be [B, T, K, H] for q's B and T")
+    return _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, return_lse, out,
+                 ws, T, new_rows=(k_new, v_new))
 
 
 def gather(cache: Cache, seq_lens, max_seq_len):

@@ -23,7 +23,13 @@ constexpr int MAX_B = 4096;            // sequences per call (per-workgroup LDS 
 // the rows); more rows go to the matrix cores.
 constexpr int valu_max_rows(int H) { return H == 64 ? 8 : 4; }
 constexpr int MFMA_MAX_NB = 4;         // 16-row blocks per matrix-core unit
-constexpr int MIN_STEPS_PER_WORKER = 2;  // do not spread fewer 128-token steps over a workgroup
+// An automatic grid gives every unit a worker of its own. Units of at most
+// SHORT_UNIT_STEPS 128-token steps are never split: a split adds a partial
+// and a merge (a chain of memory round trips), which costs more than the
+// shorter stream saves. Longer units are split as far as every worker keeps
+// MIN_STEPS_PER_WORKER steps.
+constexpr int SHORT_UNIT_STEPS = 4;
+constexpr int MIN_STEPS_PER_WORKER = 2;
 // Resident workgroups per CU at the kernels' register use (vector-ALU kernel:
 // 2 waves per SIMD; matrix-core kernel: 1), so an automatic grid is one
 // round of workgroups.
@@ -89,7 +95,11 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
   } else {
     const int64_t steps_ub = units * ((max_seq_len + kvc::STEP - 1) / kvc::STEP);
     const int64_t full = (int64_t)device_cu_count() * (p->mfma ? MFMA_WG_PER_CU : VALU_WG_PER_CU);
-    const int64_t want_workers = (steps_ub + MIN_STEPS_PER_WORKER - 1) / MIN_STEPS_PER_WORKER;
+    const int64_t unit_steps = (max_seq_len + kvc::STEP - 1) / kvc::STEP;
+    int64_t want_workers = unit_steps <= SHORT_UNIT_STEPS
+                               ? units
+                               : (steps_ub + MIN_STEPS_PER_WORKER - 1) / MIN_STEPS_PER_WORKER;
+    if (want_workers < units) want_workers = units;
     int64_t want = (want_workers + per_wg - 1) / per_wg;
     if (want > full) want = full;
     p->W = (int)(want < 1 ? 1 : want);
@@ -134,9 +144,36 @@ kvc_status check_cache(const kvc_cache* c, int K, int H, int* capacity, int* shi
   return KVC_OK;
 }
 
+// Fills the copy arguments of an append (shared by kvc_append and the fused
+// entry point's two-launch form).
+void fill_copy_args(CopyArgs* a, const kvc_cache* c, int capacity, int shift, const void* k_new,
+                    const void* v_new, int B, int T, int K, int H, const int32_t* seq_lens) {
+  memset(a, 0, sizeof(*a));
+  a->k = static_cast<char*>(c->k);
+  a->v = static_cast<char*>(c->v);
+  a->table = c->block_table;
+  a->stride_seq = c->stride_seq * 2;
+  a->stride_head = c->stride_head * 2;
+  a->stride_tok = c->stride_tok * 2;
+  a->capacity = capacity;
+  a->block_shift = shift;
+  a->max_blocks = c->block_table ? c->max_blocks_per_seq : 0;
+  a->num_blocks = c->block_table ? c->num_blocks : 0;
+  a->k_new = static_cast<const char*>(k_new);
+  a->v_new = static_cast<const char*>(v_new);
+  a->seq_lens = seq_lens;
+  a->B = B;
+  a->T = T;
+  a->K = K;
+  a->H = H;
+}
+
+// Attention, optionally preceded by the append of k_new / v_new (fused: one
+// launch when every (b, k) is one unit, else an append launch first).
 kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dtype, float* lse,
                        int B, int T, int N, int K, int H, const int32_t* seq_lens, int max_seq_len,
-                       float scale, int num_wg, void* ws, size_t ws_bytes, void* stream) {
+                       float scale, int num_wg, void* ws, size_t ws_bytes, void* stream,
+                       const void* k_new = nullptr, const void* v_new = nullptr) {
   int capacity = 0, shift = 0;
   const kvc_status st = check_cache(c, K, H, &capacity, &shift);
   if (st != KVC_OK) return st;
@@ -148,6 +185,8 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   if (B == 0) return KVC_OK;  // nothing to read or write; empty buffers may be null
   if (!q || !out || !seq_lens) return KVC_ERR_INVALID;
   if (!aligned16(q) || !aligned16(out)) return KVC_ERR_INVALID;
+  const bool fused = k_new != nullptr || v_new != nullptr;
+  if (fused && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return KVC_ERR_INVALID;
   if ((int64_t)B * K * ((N / K * T + 63) / 64) > COUNTER_SLOTS) return KVC_ERR_UNSUPPORTED;
   Plan p;
   if (!make_plan(B, T, N, K, H, max_seq_len, num_wg, &p)) return KVC_ERR_INVALID;
@@ -188,6 +227,16 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   const bool bf = c->dtype == KVC_BF16;
   const bool paged = c->block_table != nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused && p.RB == 1) {
+    a.k_new = static_cast<const char*>(k_new);
+    a.v_new = static_cast<const char*>(v_new);
+    a.k_store = static_cast<char*>(c->k);
+    a.v_store = static_cast<char*>(c->v);
+  } else if (fused) {
+    CopyArgs ca;
+    fill_copy_args(&ca, c, capacity, shift, k_new, v_new, B, T, K, H, seq_lens);
+    if (kvc::launch_append(ca, paged, s) != hipSuccess) return KVC_ERR_HIP;
+  }
   const hipError_t e = p.mfma ? kvc::launch_attn_mfma(a, bf, H, paged, s)
                               : kvc::launch_attn_valu(a, bf, H, paged, s);
   return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
@@ -207,24 +256,7 @@ kvc_status kvc_append(const kvc_cache* cache, const void* k_new, const void* v_n
   if (!k_new || !v_new || !seq_lens) return KVC_ERR_INVALID;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVC_ERR_INVALID;
   CopyArgs a;
-  memset(&a, 0, sizeof(a));
-  a.k = static_cast<char*>(cache->k);
-  a.v = static_cast<char*>(cache->v);
-  a.table = cache->block_table;
-  a.stride_seq = cache->stride_seq * 2;
-  a.stride_head = cache->stride_head * 2;
-  a.stride_tok = cache->stride_tok * 2;
-  a.capacity = capacity;
-  a.block_shift = shift;
-  a.max_blocks = cache->block_table ? cache->max_blocks_per_seq : 0;
-  a.num_blocks = cache->block_table ? cache->num_blocks : 0;
-  a.k_new = static_cast<const char*>(k_new);
-  a.v_new = static_cast<const char*>(v_new);
-  a.seq_lens = seq_lens;
-  a.B = B;
-  a.T = T;
-  a.K = K;
-  a.H = H;
+  fill_copy_args(&a, cache, capacity, shift, k_new, v_new, B, T, K, H, seq_lens);
   const hipError_t e = kvc::launch_append(a, cache->block_table != nullptr, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
@@ -243,6 +275,16 @@ kvc_status kvc_attn_verify(const kvc_cache* cache, const void* q, void* out, int
                            size_t workspace_bytes, void* stream) {
   return attn_common(cache, q, out, out_dtype, lse, B, T, N, K, H, seq_lens, max_seq_len, scale,
                      num_workgroups, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_append_attend(const kvc_cache* cache, const void* k_new, const void* v_new,
+                             const void* q, void* out, int out_dtype, float* lse, int B, int T,
+                             int N, int K, int H, const int32_t* seq_lens, int max_seq_len,
+                             float scale, int num_workgroups, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return KVC_ERR_INVALID;
+  return attn_common(cache, q, out, out_dtype, lse, B, T, N, K, H, seq_lens, max_seq_len, scale,
+                     num_workgroups, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 size_t kvc_workspace_bytes(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups) {

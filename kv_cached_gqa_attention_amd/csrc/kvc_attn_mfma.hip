@@ -104,9 +104,10 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a);
   const Partition part = make_partition(a, s_pre, blockIdx.x);
+  append_owned<H, THREADS, PAGED>(a, s_pre, part);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int c = lane & 15;   // column (query row) / A-row (token or h) within a 16 block
   const int g = lane >> 4;   // k-slot group
   const int i8 = lane & 7;   // lane within its transpose octet
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    finish_segment<H, 1>(a, s, blockIdx.x, s_m, s_l, s_o, segbad, shared);
+    finish_segment<H, 1>(a, s, blockIdx.x, s_m, s_l, s_o, s_m, segbad, shared);
   }
   count_and_merge<H>(a, shared, s_flag);
 }

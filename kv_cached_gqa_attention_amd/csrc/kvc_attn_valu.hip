@@ -47,15 +47,17 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
   extern __shared__ int32_t s_pre[];   // [2B + 1]
   __shared__ float s_m[WAVES * R], s_l[WAVES * R];
   __shared__ float s_o[WAVES * R * H];
+  __shared__ float s_w[(WAVES + 2) * R];
   __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[2];
 
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a);
   const Partition part = make_partition(a, s_pre, blockIdx.x);
+  append_owned<H, THREADS, PAGED>(a, s_pre, part);
   if (part.lo >= part.hi) return;  // the whole workgroup: no barrier is skipped
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int grp = lane / LPR;
   const int li = lane % LPR;
   const int lane_off = li * 16;  // byte offset of this lane's first 8 dims in a row
@@ -241,20 +243,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
     // ---- combine this wave's lane groups, park the wave's state in LDS
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float mr = m[r];
-#pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) mr = fmaxf(mr, shfl_xor_f(mr, msk));
+      static_assert(LPR == 8, "lane groups of 8: the reductions run over 8 groups");
+      const float mr = max_groups8(m[r]);
       const float scl = __builtin_amdgcn_exp2f(m[r] - mr);
-      float lr = l[r] * scl;
+      const float lr = sum_groups8(l[r] * scl);
 #pragma unroll
-      for (int msk = LPR; msk < 64; msk <<= 1) lr += shfl_xor_f(lr, msk);
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) {
-        float od = o[r][d] * scl;
-#pragma unroll
-        for (int msk = LPR; msk < 64; msk <<= 1) od += shfl_xor_f(od, msk);
-        o[r][d] = od;
-      }
+      for (int d = 0; d < DPL; ++d) o[r][d] = sum_groups8(o[r][d] * scl);
       // lane group g parks rows g, g + GROUPS, ...
       if (r % GROUPS == grp) {
 #pragma unroll
@@ -277,7 +271,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
     // The next unit's first tiles are in flight while the workgroup combines
     // and writes this one.
-    finish_segment<H, WAVES>(a, cur, blockIdx.x, s_m, s_l, s_o, segbad, shared);
+    finish_segment<H, WAVES>(a, cur, blockIdx.x, s_m, s_l, s_o, s_w, segbad, shared);
 
     if (!has_next) break;
     cur = nxt;
@@ -293,10 +287,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
 template <bool BF, int H, int R, bool PAGED>
 static hipError_t launch_valu_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int LPR = 8;
-  // Two waves per SIMD where the main loop still fits without spilling
-  // (a few spills outside the loop are cheap); otherwise let the compiler
-  // take the registers it wants.
-  constexpr int WPE = (H == 128 && R <= 4) || (H == 64 && R <= 6) ? 2 : 1;
+  // Two waves per SIMD (at most 256 registers per lane) wherever the loop
+  // fits without spilling: every shape except H = 128 with more than four
+  // rows, which goes to the matrix cores anyway.
+  constexpr int WPE = (H == 128 && R <= 4) || H == 64 ? 2 : 1;
   const size_t shmem = (size_t)(2 * a.B + 1) * sizeof(int32_t);
   // one worker per workgroup; its waves interleave the tiles
   hipLaunchKernelGGL((attn_valu_kernel<BF, H, R, LPR, PAGED, WPE>), dim3(a.W), dim3(THREADS),

@@ -68,6 +68,13 @@ struct AttnArgs {
   float* part_o;      // [W + units, RMAX, H], slot = worker + unit
   float* part_ml;     // [W + units, RMAX, 2]
   int32_t* counters;  // [units]
+  // Fused append (nullptr otherwise): the T new rows of every (b, k),
+  // [B, T, K, H] in the cache dtype, which the kernel writes into the cache
+  // before attending (append_owned).
+  const char* k_new;
+  const char* v_new;
+  char* k_store;  // the K and V caches again, writable
+  char* v_store;
 };
 
 // ---------------------------------------------------------------- dtypes
@@ -174,6 +181,30 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) {
   return __shfl_xor(x, m, 64);
+}
+
+// Reductions over the eight aligned groups of 8 lanes (lane l with l ^ 8,
+// l ^ 16, l ^ 32): a DPP rotate by 8 within each 16-lane row (= xor 8), an
+// LDS-free swizzle swapping 16-lane halves of each 32 lanes (= xor 16), and a
+// swap of the wave's two 32-lane halves (the pair it returns is {x[l],
+// x[l ^ 32]} in every lane). Every lane gets the same sum, in the same order.
+__device__ __forceinline__ float xor8_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float xor16_f(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+__device__ __forceinline__ float sum_groups8(float x) {
+  x += xor8_f(x);
+  x += xor16_f(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_groups8(float x) {
+  x = fmaxf(x, xor8_f(x));
+  x = fmaxf(x, xor16_f(x));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // ---------------------------------------------------------------- partition
@@ -296,6 +327,48 @@ __device__ __forceinline__ Segment find_segment(const AttnArgs& a, const int32_t
   return s;
 }
 
+// ---------------------------------------------------------------- fused append
+
+// The fused append's share of this workgroup: every new row that lies in one
+// of its own steps, copied in 16-byte chunks to its logical position exactly
+// as the separate append does (rows of an out-of-range block entry are
+// skipped; sequences of invalid length own no steps). Each new row is read
+// only by the workgroup owning its step (and the clamped reads past a
+// sequence's end hit its last row, in the same step), so after this
+// workgroup's stores are acknowledged and its waves have met, its own reads
+// see them and no other workgroup reads them. Requires one row block per
+// (b, k): with several, other workgroups would read the rows too.
+template <int H, int NT, bool PAGED>
+__device__ void append_owned(const AttnArgs& a, const int32_t* s_pre, const Partition& part) {
+  if (!a.k_new) return;
+  constexpr int CPR = H / 8;  // 16-byte chunks per row
+  for (int64_t x = part.lo; x < part.hi;) {
+    const Segment g = find_segment(a, s_pre, part, x);
+    x += g.t_end - g.t_begin;
+    const int new0 = g.seq_len - a.T;
+    const int lo = max(new0, g.t_begin * STEP);
+    const int hi = min(g.seq_len, g.t_end * STEP);
+    for (int e = threadIdx.x; e < (hi - lo) * CPR; e += NT) {
+      const int pos = lo + e / CPR;
+      const int ch = e - (e / CPR) * CPR;
+      int64_t off;
+      if constexpr (PAGED) {
+        const int blk = a.table[(int64_t)g.b * a.max_blocks + (pos >> a.block_shift)];
+        if ((unsigned)blk >= (unsigned)a.num_blocks) continue;
+        off = (int64_t)blk * a.stride_seq + (int64_t)(pos & ((1 << a.block_shift) - 1)) * a.stride_tok;
+      } else {
+        off = (int64_t)g.b * a.stride_seq + (int64_t)pos * a.stride_tok;
+      }
+      off += (int64_t)g.k * a.stride_head + ch * 16;
+      const int64_t src = (((int64_t)g.b * a.T + (pos - new0)) * a.K + g.k) * (H * 2) + ch * 16;
+      *reinterpret_cast<uint4*>(a.k_store + off) = *reinterpret_cast<const uint4*>(a.k_new + src);
+      *reinterpret_cast<uint4*>(a.v_store + off) = *reinterpret_cast<const uint4*>(a.v_new + src);
+    }
+  }
+  wait_stores();
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- outputs
 
 __device__ __forceinline__ int64_t row_index(const AttnArgs& a, int b, int k, int r) {
@@ -334,7 +407,7 @@ __device__ void fill_invalid(const AttnArgs& a) {
 
 // Finishing one unit segment whose per-wave states sit in LDS:
 //   s_m[w * RMAX + r], s_l[w * RMAX + r], s_o[(w * RMAX + r) * H + h]
-// for NW wave states. The waves' states are combined, then either the output
+// for NW wave states (s_w: LDS for the per-row combination, [NW + 2][RMAX]). The waves' states are combined, then either the output
 // is written (the segment is the whole unit: finish_direct) or a partial is
 // stored (store_partial). A worker's shared units are counted together once
 // its whole range is done (count_and_merge): the workgroup that counts a
@@ -343,19 +416,47 @@ __device__ void fill_invalid(const AttnArgs& a) {
 // end, keeps both latencies out of the middle of the range. `bad` marks a
 // segment that met an out-of-range block-table entry: its result is NaN.
 
-// Combined state of the NW waves for (row r, dim h).
+// Per row r < rows: the largest of the NW waves' maxima, each wave's weight
+// 2^(m_w - M) and the combined sum, into s_w ([NW + 2][RMAX] floats: weights,
+// then M, then L). With one wave there is nothing to combine. Ends with a
+// barrier when it writes.
+template <int NW>
+__device__ __forceinline__ void combine_rows(const AttnArgs& a, int rows, const float* s_m,
+                                             const float* s_l, float* s_w) {
+  if constexpr (NW > 1) {
+    for (int r = threadIdx.x; r < rows; r += THREADS) {
+      float M = NEG_BIG;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * a.RMAX + r]);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float wt = __builtin_amdgcn_exp2f(s_m[w * a.RMAX + r] - M);
+        s_w[w * a.RMAX + r] = wt;
+        L += wt * s_l[w * a.RMAX + r];
+      }
+      s_w[NW * a.RMAX + r] = M;
+      s_w[(NW + 1) * a.RMAX + r] = L;
+    }
+    __syncthreads();
+  }
+}
+
+// Combined state of the NW waves for (row r, dim h), after combine_rows.
 template <int H, int NW>
 __device__ __forceinline__ void combine_waves(const AttnArgs& a, const float* s_m, const float* s_l,
-                                              const float* s_o, int r, int h, float& M, float& L,
-                                              float& O) {
-  M = NEG_BIG;
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * a.RMAX + r]);
-  L = 0.f;
-  O = 0.f;
-  for (int w = 0; w < NW; ++w) {
-    const float sc = exp2f(s_m[w * a.RMAX + r] - M);
-    L += sc * s_l[w * a.RMAX + r];
-    O += sc * s_o[(w * a.RMAX + r) * H + h];
+                                              const float* s_o, const float* s_w, int r, int h,
+                                              float& M, float& L, float& O) {
+  if constexpr (NW == 1) {
+    M = s_m[r];
+    L = s_l[r];
+    O = s_o[r * H + h];
+  } else {
+    M = s_w[NW * a.RMAX + r];
+    L = s_w[(NW + 1) * a.RMAX + r];
+    O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) O += s_w[w * a.RMAX + r] * s_o[(w * a.RMAX + r) * H + h];
   }
 }
 
@@ -363,14 +464,15 @@ __device__ __forceinline__ void combine_waves(const AttnArgs& a, const float* s_
 // LDS may be reused afterwards.
 template <int H, int NW>
 __device__ void finish_direct(const AttnArgs& a, const Segment& s, const float* s_m,
-                              const float* s_l, const float* s_o, bool bad) {
+                              const float* s_l, const float* s_o, float* s_w, bool bad) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const int row0 = s.rb * a.RMAX;
   const float qnan = __int_as_float(0x7fc00000);
+  combine_rows<NW>(a, rows, s_m, s_l, s_w);
   for (int e = threadIdx.x; e < rows * H; e += THREADS) {
     const int r = e / H, h = e - (e / H) * H;
     float M, L, O;
-    combine_waves<H, NW>(a, s_m, s_l, s_o, r, h, M, L, O);
+    combine_waves<H, NW>(a, s_m, s_l, s_o, s_w, r, h, M, L, O);
     if (bad) O = L = M = qnan;
     write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
   }
@@ -383,16 +485,17 @@ __device__ void finish_direct(const AttnArgs& a, const Segment& s, const float* 
 // afterwards.
 template <int H, int NW>
 __device__ void store_partial(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
-                              const float* s_l, const float* s_o, bool bad) {
+                              const float* s_l, const float* s_o, float* s_w, bool bad) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const float qnan = __int_as_float(0x7fc00000);
   const int slot = worker + s.unit;
   float* po = a.part_o + (int64_t)slot * a.RMAX * H;
   float* pml = a.part_ml + (int64_t)slot * a.RMAX * 2;
+  combine_rows<NW>(a, rows, s_m, s_l, s_w);
   for (int e = threadIdx.x; e < rows * H; e += THREADS) {
     const int r = e / H, h = e - (e / H) * H;
     float M, L, O;
-    combine_waves<H, NW>(a, s_m, s_l, s_o, r, h, M, L, O);
+    combine_waves<H, NW>(a, s_m, s_l, s_o, s_w, r, h, M, L, O);
     if (bad) O = L = M = qnan;
     store_coherent(po + r * H + h, O);
     if (h == 0) {
@@ -479,11 +582,12 @@ struct SharedUnits {
 // end. Ends with a barrier, so LDS may be reused afterwards.
 template <int H, int NW>
 __device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
-                               const float* s_l, const float* s_o, bool bad, SharedUnits& sh) {
+                               const float* s_l, const float* s_o, float* s_w, bool bad,
+                               SharedUnits& sh) {
   if (s.n_parts == 1) {
-    finish_direct<H, NW>(a, s, s_m, s_l, s_o, bad);
+    finish_direct<H, NW>(a, s, s_m, s_l, s_o, s_w, bad);
   } else {
-    store_partial<H, NW>(a, s, worker, s_m, s_l, s_o, bad);
+    store_partial<H, NW>(a, s, worker, s_m, s_l, s_o, s_w, bad);
     sh.add(s);
   }
 }

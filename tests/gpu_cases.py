@@ -48,7 +48,10 @@ def build_cache(inp, layout, seed, block_size=16, extra_blocks=3, capacity=None,
 
 def run_case(B, T, N, K, H, dtype, prior, layout="contiguous", seed=1, num_workgroups=0,
              out_dtype=torch.float32, block_size=16, scale=None, device="cuda", draw_device="cpu",
-             capacity=None):
+             capacity=None, fused=False):
+    """Build the cache from the prior rows, then append the new rows and attend:
+    two calls (append, then decode/verify) or, with ``fused``, one
+    append_attend call."""
     prior = np.asarray(prior, dtype=np.int64)
     say(f"case B={B} T={T} N={N} K={K} H={H} {dtype} {layout} prior[max]={int(prior.max(initial=0))} "
         f"seed={seed} wg={num_workgroups}")
@@ -57,9 +60,18 @@ def run_case(B, T, N, K, H, dtype, prior, layout="contiguous", seed=1, num_workg
         inp = to_device(inp, device)
     cache, table = build_cache(inp, layout, seed, block_size=block_size, capacity=capacity)
     seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(device)
-    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
     max_len = int(inp.seq_lens.max())
     scale = 1.0 / math.sqrt(H) if scale is None else scale
+    if fused:
+        q = inp.q[:, 0].contiguous() if T == 1 else inp.q
+        out, lse = kvc.append_attend(q, inp.k_new, inp.v_new, cache, seq_lens, max_len, scale=scale,
+                                     out_dtype=out_dtype, num_workgroups=num_workgroups,
+                                     return_lse=True)
+        if T == 1:
+            out, lse = out[:, None], lse[:, None]
+        torch.cuda.synchronize()
+        return Run(inp, cache, seq_lens, out, lse, scale, table)
+    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
     if T == 1:
         out, lse = kvc.decode(inp.q[:, 0].contiguous(), cache, seq_lens, max_len, scale=scale,
                               out_dtype=out_dtype, num_workgroups=num_workgroups, return_lse=True)

@@ -146,3 +146,32 @@ def test_verify_and_append_host_errors(lib):
     assert ap(B=0) == E.KVC_OK
     g = lambda cc: lib.kvc_gather(ctypes.byref(cc), FAKE, FAKE, 0, 8, 128, FAKE, 16, None)
     assert g(c) == E.KVC_ERR_INVALID  # gather needs a paged cache
+
+
+def test_append_attend_host_errors(lib):
+    E = _lib
+    c = _cache()
+
+    def aa(**kw):
+        return lib.kvc_append_attend(ctypes.byref(kw.get("c", c)), kw.get("kn", FAKE),
+                                     kw.get("vn", FAKE), kw.get("q", FAKE), FAKE, E.KVC_F32, None,
+                                     kw.get("B", 8), kw.get("T", 1), kw.get("N", 64), 8,
+                                     kw.get("H", 128), FAKE, kw.get("L", 4096), 0.1, 0,
+                                     kw.get("ws", FAKE), 1 << 30, None)
+
+    # everything the two separate calls reject is rejected before any launch
+    assert aa(kn=None) == E.KVC_ERR_INVALID
+    assert aa(vn=None) == E.KVC_ERR_INVALID
+    assert aa(kn=FAKE + 4) == E.KVC_ERR_INVALID
+    assert aa(vn=FAKE + 8) == E.KVC_ERR_INVALID
+    assert aa(T=0) == E.KVC_ERR_INVALID
+    assert aa(T=17) == E.KVC_ERR_INVALID
+    assert aa(N=60) == E.KVC_ERR_INVALID
+    assert aa(H=80) == E.KVC_ERR_UNSUPPORTED
+    assert aa(L=4097) == E.KVC_ERR_INVALID
+    assert aa(q=None) == E.KVC_ERR_INVALID
+    assert aa(ws=None) == E.KVC_ERR_WORKSPACE
+    assert aa(c=_cache(dtype=E.KVC_F32)) == E.KVC_ERR_UNSUPPORTED
+    # an empty batch is a successful no-op, with or without buffers
+    assert aa(B=0) == E.KVC_OK
+    assert aa(B=0, kn=None, vn=None, q=None) == E.KVC_OK

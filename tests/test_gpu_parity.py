@@ -269,3 +269,115 @@ def test_one_workspace_serves_calls_of_any_shape(gpu_device):
                     o_ref, _ = oracle_unit(inp, b, k, 1 / math.sqrt(H))
                     got = out[b, :, k * G : (k + 1) * G].double().cpu().numpy()
                     assert np.abs(got - o_ref).max() <= 2e-3, (rep, B, T, N, K, H)
+
+
+# ----------------------------------------------------------------- fused append + attend
+
+FUSED = [SMALL[0], SMALL[3], SMALL[5], SMALL[7], SMALL[9], SMALL[11], SMALL[12], SMALL[13]]
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("case", FUSED, ids=_ids(FUSED))
+def test_fused_append_attend_matches_oracle_and_separate_calls(gpu_device, case, layout):
+    """One append_attend call: outputs match the oracle, and the cache and the
+    outputs are bit-equal to those of append followed by decode/verify (the
+    kernels see the same rows in the same order). G*T = 128 (two row blocks)
+    takes the two-launch form."""
+    B, T, N, K, H, dtype, prior = case
+    kw = dict(layout=layout, seed=300 + B * 7 + T, num_workgroups=0)
+    fused = run_case(B, T, N, K, H, dtype, prior, fused=True, **kw)
+    compare_units(fused, all_units(fused.inp))
+    sep = run_case(B, T, N, K, H, dtype, prior, **kw)
+    assert torch.equal(fused.cache.k.view(torch.int16), sep.cache.k.view(torch.int16))
+    assert torch.equal(fused.cache.v.view(torch.int16), sep.cache.v.view(torch.int16))
+    assert torch.equal(fused.out, sep.out) and torch.equal(fused.lse, sep.lse)
+
+
+@pytest.mark.parametrize("nwg", [1, 3, 0, 5000])
+def test_fused_any_workgroup_count(gpu_device, nwg):
+    """New rows land in steps owned by different workgroups as the grid changes."""
+    for T, N, K in [(1, 32, 8), (5, 64, 8), (13, 4, 1)]:
+        run = run_case(3, T, N, K, 128, BF, [126, 0, 2000], seed=81, num_workgroups=nwg, fused=True)
+        compare_units(run, all_units(run.inp))
+
+
+def test_fused_invalid_lengths_skip_append_and_give_nan(gpu_device):
+    B, T, N, K, H = 4, 2, 8, 2, 64
+    inp = draw_inputs(B, T, N, K, H, HF, np.array([10, 20, 30, 40]), 83, device="cpu")
+    dev = gpu_device
+    for name in ("q", "k_new", "v_new", "ctx_k", "ctx_v"):
+        setattr(inp, name, getattr(inp, name).to(dev))
+    ck, cv = layout_contiguous(inp, capacity=64, pad_value=0.0)
+    cache = kvc.Cache(ck, cv)
+    lens = inp.seq_lens.astype(np.int32).copy()
+    lens[1] = 65  # beyond capacity
+    lens[2] = 1   # shorter than T
+    seq_lens = torch.from_numpy(lens).to(dev)
+    before_k = cache.k.clone()
+    out = kvc.append_attend(inp.q, inp.k_new, inp.v_new, cache, seq_lens, 64,
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in (1, 2):
+        assert torch.isnan(out[b]).all()
+        assert torch.equal(cache.k[b].view(torch.int16), before_k[b].view(torch.int16))
+    for b in (0, 3):
+        assert torch.isfinite(out[b]).all()
+        p = int(lens[b]) - T
+        assert torch.equal(cache.k[b, :, p:p + T].view(torch.int16),
+                           inp.k_new[b].transpose(0, 1).view(torch.int16))
+
+
+def test_graph_replays_match_eager(gpu_device):
+    """A captured fused step (append_attend) and a captured verify, replayed
+    several times with eager calls and synchronizations in between: every
+    replay equals the eager result bitwise (the calls record no memset; the
+    workspace counters are left zero by every call)."""
+    dev = gpu_device
+    results = []
+    for T, N, K in [(1, 32, 8), (5, 64, 8)]:
+        B, H = 4, 128
+        inp = draw_inputs(B, T, N, K, H, BF, np.array([700, 3, 1500, 64]), 91, device="cpu")
+        for name in ("q", "k_new", "v_new", "ctx_k", "ctx_v"):
+            setattr(inp, name, getattr(inp, name).to(dev))
+        ck, cv = layout_contiguous(inp, pad_value=float("nan"))
+        cache = kvc.Cache(ck, cv)
+        seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(dev)
+        L = int(inp.seq_lens.max())
+        q = inp.q[:, 0].contiguous() if T == 1 else inp.q
+        ws = torch.zeros(kvc.workspace_bytes(B, T, N, K, H, L, 0), dtype=torch.uint8, device=dev)
+        out_g = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        out_v = torch.empty(q.shape, dtype=torch.float32, device=dev)
+
+        def fused_call(out):
+            kvc.append_attend(q, inp.k_new, inp.v_new, cache, seq_lens, L, out=out,
+                              out_dtype=torch.float32, ws=ws)
+
+        def attend_call(out):
+            f = kvc.decode if T == 1 else kvc.verify
+            f(q, cache, seq_lens, L, out=out, out_dtype=torch.float32, ws=ws)
+
+        fused_call(out_g)
+        torch.cuda.synchronize()
+        eager_fused = out_g.clone()
+        attend_call(out_v)
+        torch.cuda.synchronize()
+        eager_attend = out_v.clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        with torch.cuda.graph(g, stream=side):
+            fused_call(out_g)
+            attend_call(out_v)
+        other = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        for rep in range(4):
+            out_g.fill_(0.0)
+            out_v.fill_(0.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out_g, eager_fused), f"replay {rep}: fused output differs"
+            assert torch.equal(out_v, eager_attend), f"replay {rep}: attend output differs"
+            attend_call(other)  # eager work between replays, same workspace
+            torch.cuda.synchronize()
+            assert torch.equal(other, eager_attend)
+        results.append(float(out_g.abs().max()))
+    say(f"  graph replays ok, max|out| {results}")
