@@ -18,9 +18,15 @@ Everything here is the plain definition, in float64, written from these pages:
   position 8); a cached step builds one 1 x n score row instead of the n x n
   matrix; the bytes-per-token formula checked against the allocator.
 
+* "CS336, lectures 10 and 12", section "Reducing the KV cache", and
+  "Stanford CS336 Day 13 - Inference", section "Local Attention": local
+  attention looks at the most recent k tokens only.
+* "Accelerating Sonar through speculation", section "EAGLE": draft trees are
+  verified with custom attention masks among the new tokens.
+
 Readings where the pages are silent (the softmax scale, the head mapping,
-the mask inside a verify block, natural-log LSE) are stated where they are
-used.
+the mask inside a verify block, the window's edge, the tree mask's form,
+natural-log LSE) are stated where they are used.
 
 Pins: every function here is checked by ``tests/test_oracle.py`` against
 closed forms, brute force, the full causal recompute and the byte counts
@@ -30,10 +36,14 @@ the pages print (fixtures in ``tests/golden/``). No function is unpinned.
 from .attention import attend, attend_one_row
 from .brute import brute_attend
 from .cache_bytes import kv_cache_bytes, score_bytes
+from .masks import ancestor_words, causal_tree_words, visible_keys
 from .recompute import full_recompute
 from .split_merge import merge_partials, split_attend_row
 
 __all__ = [
+    "ancestor_words",
+    "causal_tree_words",
+    "visible_keys",
     "attend",
     "attend_one_row",
     "brute_attend",

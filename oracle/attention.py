@@ -23,12 +23,16 @@ here (callers default to 1/sqrt(H)), and scale = 1 is the pages' literal
 product.
 
 Softmax and output: m = max_j s_j, Z = sum_j exp(s_j - m),
-o = sum_j exp(s_j - m) / Z * v_j, lse = m + ln Z (natural log).
+o = sum_j exp(s_j - m) / Z * v_j, lse = m + ln Z (natural log), the sums
+running over the visible keys (oracle.masks: causal by default, optionally a
+sliding window or a draft-tree mask among the new tokens).
 """
 
 from __future__ import annotations
 
 import numpy as np
+
+from .masks import visible_keys
 
 
 def attend_one_row(q_vec: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float):
@@ -45,13 +49,16 @@ def attend_one_row(q_vec: np.ndarray, keys: np.ndarray, values: np.ndarray, scal
     return o, m + np.log(z)
 
 
-def attend(q: np.ndarray, k_seqs, v_seqs, scale: float):
+def attend(q: np.ndarray, k_seqs, v_seqs, scale: float, window: int = 0, tree_words=None):
     """Cached attention for a batch.
 
     q: float64 [B, T, N, H].
     k_seqs, v_seqs: length-B sequences of float64 [L_b, K, H], the logical
     cache of each sequence after the T new rows were appended (prior rows
     first, then the T new rows).
+    window: 0, or the sliding-window length (see oracle.masks).
+    tree_words: None (causal inside the block), or per sequence a length-T
+    list of mask words (see oracle.masks).
     Returns (out float64 [B, T, N, H], lse float64 [B, T, N]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -71,10 +78,11 @@ def attend(q: np.ndarray, k_seqs, v_seqs, scale: float):
         G = N // K
         P = L - T
         for t in range(T):
-            visible = P + t + 1
+            word = None if tree_words is None else int(tree_words[b][t])
+            vis = visible_keys(P, T, t, window, word)
             for n in range(N):
                 k = n // G
-                o, l = attend_one_row(q[b, t, n], kb[:visible, k, :], vb[:visible, k, :], scale)
+                o, l = attend_one_row(q[b, t, n], kb[vis, k, :], vb[vis, k, :], scale)
                 out[b, t, n] = o
                 lse[b, t, n] = l
     return out, lse

@@ -15,13 +15,16 @@ import pytest
 import torch
 
 from oracle import (
+    ancestor_words,
     attend,
+    causal_tree_words,
     brute_attend,
     full_recompute,
     kv_cache_bytes,
     merge_partials,
     score_bytes,
     split_attend_row,
+    visible_keys,
 )
 from workloads import draw_inputs, layout_contiguous
 
@@ -317,3 +320,117 @@ def test_attend_rejects_bad_shapes():
         attend(q, [np.zeros((1, 1, 4))], [np.zeros((1, 1, 4))], 1.0)  # L < T
     with pytest.raises(ValueError):
         attend(q, [np.zeros((4, 2, 4))], [np.zeros((4, 2, 4))], 1.0)  # N % K
+
+
+# --------------------------------------------------------------------------- masks
+
+
+def _visibility_pattern(P, T, window=0, words=None):
+    """With q = 0 every visible score is equal, so out = mean of the visible
+    values; one-hot values (value of key j = e_j) turn the mean into 1/|V| on
+    exactly the visible keys. Returns the [T, L] pattern the oracle computed."""
+    L = P + T
+    q = np.zeros((1, T, 1, L))
+    k = np.zeros((L, 1, L))
+    v = np.eye(L).reshape(L, 1, L)
+    out, _ = attend(q, [k], [v], 1.0, window=window, tree_words=None if words is None else [words])
+    return out[0, :, 0, :]
+
+
+@pytest.mark.parametrize("P,T,W", [(0, 1, 1), (5, 1, 1), (5, 1, 3), (5, 1, 6), (5, 1, 50), (9, 4, 1),
+                                   (9, 4, 2), (9, 4, 5), (9, 4, 13), (3, 5, 4), (0, 5, 2)])
+def test_window_sees_exactly_the_last_w_positions(P, T, W):
+    """Catches an off-by-one at either edge of the window: position i sees
+    max(0, i - W + 1) .. i, i.e. min(W, i + 1) keys (worked by hand)."""
+    pat = _visibility_pattern(P, T, window=W)
+    for t in range(T):
+        i = P + t
+        lo = max(0, i - W + 1)
+        want = np.zeros(P + T)
+        want[lo : i + 1] = 1.0 / (i + 1 - lo)
+        assert np.allclose(pat[t], want, rtol=0, atol=1e-15), (t, pat[t])
+
+
+def test_window_one_returns_the_own_value_and_score():
+    """W = 1: softmax over one key, so out = v_i exactly and lse = s_ii."""
+    rng = np.random.default_rng(3)
+    q, ks, vs = _rand_problem(rng, 2, 3, 4, 2, 8, [7, 0])
+    out, lse = attend(q, ks, vs, 0.3, window=1)
+    for b in range(2):
+        P = ks[b].shape[0] - 3
+        for t in range(3):
+            for n in range(4):
+                kv = n // 2
+                assert np.array_equal(out[b, t, n], vs[b][P + t, kv])
+                assert lse[b, t, n] == pytest.approx(0.3 * float(q[b, t, n] @ ks[b][P + t, kv]), abs=1e-12)
+
+
+def test_window_not_shorter_than_the_sequence_changes_nothing():
+    rng = np.random.default_rng(4)
+    q, ks, vs = _rand_problem(rng, 2, 2, 4, 2, 8, [20, 3])
+    full = attend(q, ks, vs, 0.25)
+    for W in (23, 24, 1000):
+        win = attend(q, ks, vs, 0.25, window=W)
+        assert np.array_equal(full[0], win[0]) and np.array_equal(full[1], win[1])
+
+
+def test_ancestor_words_by_hand():
+    """A chain gives the causal words; a star sees root and self; a small
+    tree (0 -> 1 -> 3, 0 -> 2) written out bit by bit."""
+    assert ancestor_words([-1, 0, 1, 2]) == [0b1, 0b11, 0b111, 0b1111] == causal_tree_words(4)
+    assert ancestor_words([-1, 0, 0, 0]) == [0b1, 0b11, 0b101, 0b1001]
+    assert ancestor_words([-1, 0, 0, 1]) == [0b1, 0b11, 0b101, 0b1011]
+    assert ancestor_words([-1, -1]) == [0b1, 0b10]
+    with pytest.raises(ValueError):
+        ancestor_words([-1, 2, 0])
+
+
+def test_causal_tree_words_reproduce_the_causal_rule():
+    rng = np.random.default_rng(5)
+    q, ks, vs = _rand_problem(rng, 2, 5, 6, 3, 8, [9, 0])
+    a = attend(q, ks, vs, 0.2)
+    b = attend(q, ks, vs, 0.2, tree_words=[causal_tree_words(5)] * 2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_tree_visibility_is_prior_plus_own_branch():
+    """Catches a mask applied to the prior rows or read with the wrong bit
+    order: the visible set is all P prior keys plus exactly the new keys
+    whose bit is set."""
+    P, T = 6, 5
+    words = ancestor_words([-1, 0, 0, 1, 2])
+    pat = _visibility_pattern(P, T, words=words)
+    for t in range(T):
+        vis = list(range(P)) + [P + u for u in range(T) if (words[t] >> u) & 1]
+        want = np.zeros(P + T)
+        want[vis] = 1.0 / len(vis)
+        assert np.allclose(pat[t], want, rtol=0, atol=1e-15), (t, pat[t])
+
+
+def test_star_tree_equals_attention_over_a_rebuilt_sequence():
+    """Drafts 1..T-1 all children of draft 0: draft t is the causal last
+    token of the sequence prior + [draft 0, draft t], built by hand."""
+    rng = np.random.default_rng(6)
+    P, T, N, K, H = 7, 4, 4, 2, 8
+    q, ks, vs = _rand_problem(rng, 1, T, N, K, H, [P])
+    out, lse = attend(q, ks, vs, 0.4, tree_words=[ancestor_words([-1] + [0] * (T - 1))])
+    for t in range(1, T):
+        rows = list(range(P)) + [P, P + t]
+        k2, v2 = ks[0][rows], vs[0][rows]
+        o2, l2 = attend(q[:, t : t + 1], [k2], [v2], 0.4)
+        assert np.allclose(out[0, t], o2[0, 0], rtol=0, atol=1e-13)
+        assert np.allclose(lse[0, t], l2[0, 0], rtol=0, atol=1e-13)
+
+
+def test_window_and_tree_compose():
+    """Both rules at once: the intersection of the two visible sets."""
+    P, T, W = 6, 4, 3
+    words = ancestor_words([-1, 0, 0, 2])
+    pat = _visibility_pattern(P, T, window=W, words=words)
+    for t in range(T):
+        i = P + t
+        vis = [j for j in list(range(P)) + [P + u for u in range(T) if (words[t] >> u) & 1] if j > i - W]
+        assert list(visible_keys(P, T, t, W, words[t])) == vis
+        want = np.zeros(P + T)
+        want[vis] = 1.0 / len(vis)
+        assert np.allclose(pat[t], want, rtol=0, atol=1e-15)
