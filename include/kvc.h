@@ -198,6 +198,49 @@ kvc_status kvc_append_attend(const kvc_cache *cache, const void *k_new, const vo
                              size_t workspace_bytes, void *stream);
 
 /*
+ * Options of kvc_attn. A zeroed struct (or a NULL pointer) gives exactly
+ * kvc_attn_verify.
+ *
+ * window: 0, or W >= 1 for local (sliding-window) attention ("CS336,
+ *   lectures 10 and 12", section "Reducing the KV cache": a token looks only
+ *   at the most recent tokens; "Stanford CS336 Day 13 - Inference", section
+ *   "Local Attention"): new token t, at position i = seq_lens[b] - T + t,
+ *   sees only keys at positions i - W + 1 .. i. Only the keys some query of
+ *   the call can see are read, so a call streams at most W + T - 1 (rounded
+ *   out to 128-token steps) positions per sequence and head.
+ * tree_mask: NULL for the causal rule inside the block, or device
+ *   [B, T] uint32 words for draft-tree verification ("Accelerating Sonar
+ *   through speculation", section "EAGLE": tree-shaped drafts are verified
+ *   with custom attention masks): new token t of sequence b sees new token u
+ *   exactly when bit u of tree_mask[b * T + t] is set (set t's own bit and
+ *   its ancestors'); every prior row stays visible; bits >= T are ignored.
+ *   4-byte aligned. A query that sees no key at all gets NaN.
+ *   Both options compose: a key must pass both rules.
+ * k_new, v_new: NULL, or the new rows to append first, as kvc_append_attend.
+ * reserved: must be 0.
+ */
+typedef struct {
+  const void *k_new;
+  const void *v_new;
+  const uint32_t *tree_mask;
+  int32_t window;
+  int32_t reserved;
+} kvc_attn_options;
+
+/*
+ * Attention of T >= 1 new tokens with options (window, draft-tree mask,
+ * fused append): kvc_attn_verify's arguments and rules plus opts (may be
+ * NULL). The workspace size from kvc_workspace_bytes for the same B, T, N,
+ * K, H, max_seq_len and num_workgroups is always enough (a window only
+ * lowers the need). Errors: as kvc_attn_verify and kvc_append_attend, plus
+ * KVC_ERR_INVALID for window < 0, reserved != 0 or a misaligned tree_mask.
+ */
+kvc_status kvc_attn(const kvc_cache *cache, const kvc_attn_options *opts, const void *q, void *out,
+                    int out_dtype, float *lse, int B, int T, int N, int K, int H,
+                    const int32_t *seq_lens, int max_seq_len, float scale, int num_workgroups,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Host query: workspace bytes needed by kvc_attn_decode (T = 1) or
  * kvc_attn_verify with the same B, T, N, K, H, max_seq_len and
  * num_workgroups. Returns 0 for invalid shapes. Uses the current device's

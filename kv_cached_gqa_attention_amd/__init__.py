@@ -11,6 +11,7 @@ from .api import (
     KvcError,
     append,
     append_attend,
+    attend,
     decode,
     gather,
     status_string,
@@ -24,6 +25,7 @@ __all__ = [
     "KvcError",
     "append",
     "append_attend",
+    "attend",
     "decode",
     "gather",
     "status_string",

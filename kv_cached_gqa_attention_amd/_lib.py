@@ -28,6 +28,7 @@ EXPORTS = (
     "kvc_attn_decode",
     "kvc_attn_verify",
     "kvc_append_attend",
+    "kvc_attn",
     "kvc_workspace_bytes",
     "kvc_status_string",
     "kvc_gather",
@@ -49,6 +50,18 @@ class KvcCache(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
         ("num_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class KvcAttnOptions(ctypes.Structure):
+    """Mirror of ``kvc_attn_options``."""
+
+    _fields_ = [
+        ("k_new", ctypes.c_void_p),
+        ("v_new", ctypes.c_void_p),
+        ("tree_mask", ctypes.c_void_p),
+        ("window", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -82,6 +95,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                       c_int, c_int, vp, c_int, ctypes.c_float, c_int, vp, c_size_t,
                                       vp]
     lib.kvc_append_attend.restype = c_int
+    opts_p = ctypes.POINTER(KvcAttnOptions)
+    lib.kvc_attn.argtypes = [cache_p, opts_p, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
+                             vp, c_int, ctypes.c_float, c_int, vp, c_size_t, vp]
+    lib.kvc_attn.restype = c_int
     lib.kvc_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int]
     lib.kvc_workspace_bytes.restype = c_size_t
     lib.kvc_status_string.argtypes = [c_int]

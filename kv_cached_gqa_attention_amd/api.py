@@ -159,7 +159,7 @@ def _check_new_rows(cache, k_new, v_new, seq_lens):
 
 
 def _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, return_lse, out, ws, T,
-          new_rows=None):
+          new_rows=None, opts=None):
     _gpu(q, "q")
     _gpu(seq_lens, "seq_lens")
     if not q.is_contiguous():
@@ -185,7 +185,11 @@ def _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, ret
     lib = _lib.load()
     common = (_ptr(seq_lens), int(max_seq_len), float(scale), int(num_workgroups), _ptr(ws),
               ws.numel() * ws.element_size(), _stream(q.device))
-    if new_rows is not None:
+    if opts is not None:
+        st = lib.kvc_attn(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(out), _DT[out_dtype],
+                          _ptr(lse), B, T, N, K, H, *common)
+        where = "kvc_attn"
+    elif new_rows is not None:
         k_new, v_new = new_rows
         st = lib.kvc_append_attend(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
                                    _DT[out_dtype], _ptr(lse), B, T, N, K, H, *common)
@@ -234,6 +238,40 @@ def append_attend(q, k_new, v_new, cache: Cache, seq_lens, max_seq_len, scale=No
         raise ValueError("k_new must be [B, T, K, H] for q's B and T")
     return _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, return_lse, out,
                  ws, T, new_rows=(k_new, v_new))
+
+
+def attend(q, cache: Cache, seq_lens, max_seq_len, window=0, tree_mask=None, k_new=None, v_new=None,
+           scale=None, out_dtype=None, num_workgroups=0, return_lse=False, out=None, ws=None):
+    """Attention of the new tokens with options: ``kvc_attn``.
+
+    q: [B, N, H] (one new token) or [B, T, N, H]. window: 0 or the number of
+    most recent positions each new token sees (itself included). tree_mask:
+    None (causal inside the block) or int32 [B, T] words, bit u of word
+    (b, t) = new token t sees new token u. k_new, v_new: optional rows to
+    append first ([B, T, K, H]).
+    """
+    if q.dim() not in (3, 4):
+        raise ValueError("attend takes q [B, N, H] or [B, T, N, H]")
+    T = 1 if q.dim() == 3 else q.shape[1]
+    opts = _lib.KvcAttnOptions()
+    opts.window = int(window)
+    if tree_mask is not None:
+        _gpu(tree_mask, "tree_mask")
+        if tree_mask.dtype != torch.int32 or tuple(tree_mask.shape) != (q.shape[0], T):
+            raise ValueError("tree_mask must be int32 [B, T]")
+        if not tree_mask.is_contiguous():
+            raise ValueError("tree_mask must be contiguous")
+        opts.tree_mask = _ptr(tree_mask)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _check_new_rows(cache, k_new, v_new, seq_lens)
+        if k_new.shape[0] != q.shape[0] or k_new.shape[1] != T:
+            raise ValueError("k_new must be [B, T, K, H] for q's B and T")
+        opts.k_new = _ptr(k_new)
+        opts.v_new = _ptr(v_new)
+    return _attn(q, cache, seq_lens, max_seq_len, scale, out_dtype, num_workgroups, return_lse, out,
+                 ws, T, opts=opts)
 
 
 def gather(cache: Cache, seq_lens, max_seq_len):

@@ -173,7 +173,12 @@ void fill_copy_args(CopyArgs* a, const kvc_cache* c, int capacity, int shift, co
 kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dtype, float* lse,
                        int B, int T, int N, int K, int H, const int32_t* seq_lens, int max_seq_len,
                        float scale, int num_wg, void* ws, size_t ws_bytes, void* stream,
-                       const void* k_new = nullptr, const void* v_new = nullptr) {
+                       const kvc_attn_options* opts = nullptr) {
+  const void* k_new = opts ? opts->k_new : nullptr;
+  const void* v_new = opts ? opts->v_new : nullptr;
+  const int window = opts ? opts->window : 0;
+  const uint32_t* tree = opts ? opts->tree_mask : nullptr;
+  if (opts && (opts->reserved != 0 || window < 0)) return KVC_ERR_INVALID;
   int capacity = 0, shift = 0;
   const kvc_status st = check_cache(c, K, H, &capacity, &shift);
   if (st != KVC_OK) return st;
@@ -188,8 +193,15 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   const bool fused = k_new != nullptr || v_new != nullptr;
   if (fused && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return KVC_ERR_INVALID;
   if ((int64_t)B * K * ((N / K * T + 63) / 64) > COUNTER_SLOTS) return KVC_ERR_UNSUPPORTED;
+  // a window bounds the keys any call streams per unit: at most
+  // window + T - 1 positions, starting anywhere inside a 128-token step
+  int span = max_seq_len;
+  if (window > 0) {
+    const int64_t w = (int64_t)window + T - 1 + kvc::STEP;
+    if (w < span) span = (int)w;
+  }
   Plan p;
-  if (!make_plan(B, T, N, K, H, max_seq_len, num_wg, &p)) return KVC_ERR_INVALID;
+  if (!make_plan(B, T, N, K, H, span, num_wg, &p)) return KVC_ERR_INVALID;
   if (!ws || ws_bytes < p.bytes || !aligned16(ws)) return KVC_ERR_WORKSPACE;
 
   AttnArgs a;
@@ -219,6 +231,8 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   a.out_dtype = out_dtype;
   a.W = p.workers;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.window = window;
+  a.tree = tree;
   char* w = static_cast<char*>(ws);
   a.counters = reinterpret_cast<int32_t*>(w);
   a.part_ml = reinterpret_cast<float*>(w + p.off_ml);
@@ -283,8 +297,21 @@ kvc_status kvc_append_attend(const kvc_cache* cache, const void* k_new, const vo
                              float scale, int num_workgroups, void* workspace,
                              size_t workspace_bytes, void* stream) {
   if (B > 0 && (!k_new || !v_new)) return KVC_ERR_INVALID;
+  kvc_attn_options o;
+  memset(&o, 0, sizeof(o));
+  o.k_new = k_new;
+  o.v_new = v_new;
   return attn_common(cache, q, out, out_dtype, lse, B, T, N, K, H, seq_lens, max_seq_len, scale,
-                     num_workgroups, workspace, workspace_bytes, stream, k_new, v_new);
+                     num_workgroups, workspace, workspace_bytes, stream, &o);
+}
+
+kvc_status kvc_attn(const kvc_cache* cache, const kvc_attn_options* opts, const void* q, void* out,
+                    int out_dtype, float* lse, int B, int T, int N, int K, int H,
+                    const int32_t* seq_lens, int max_seq_len, float scale, int num_workgroups,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (opts && B > 0 && opts->tree_mask && ((uintptr_t)opts->tree_mask & 3u)) return KVC_ERR_INVALID;
+  return attn_common(cache, q, out, out_dtype, lse, B, T, N, K, H, seq_lens, max_seq_len, scale,
+                     num_workgroups, workspace, workspace_bytes, stream, opts);
 }
 
 size_t kvc_workspace_bytes(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups) {

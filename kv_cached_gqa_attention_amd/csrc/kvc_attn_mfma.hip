@@ -90,7 +90,9 @@ __device__ __forceinline__ uint4 transpose8(uint4 v, int i8) {
   return make_uint4(x0, x1, x2, x3);
 }
 
-template <bool BF, int H, int NB, bool PAGED>
+// MASKED: a window or draft-tree mask is in use (the general per-key test);
+// otherwise the causal test alone.
+template <bool BF, int H, int NB, bool PAGED, bool MASKED>
 __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
   constexpr int RMAX = NB * 16;  // query rows per unit (row block)
   constexpr int KS = H / 32;     // k-steps of S^T over h
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 
     // Q^T fragments (B operand): query row rb*RMAX + 16 nb + c, h = 32 ks + 8 g + j.
     uint4 qf[NB][KS];
-    int vis[NB];
+    int tq[NB];         // new-token index of this lane's query column
+    uint32_t tw[NB];    // its tree word
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int rr = s.rb * RMAX + nb * 16 + c;
@@ -130,12 +133,13 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
         const char* qrow = a.q + row_index(a, s.b, s.k, rr) * (H * 2);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = load16(qrow + (ks * 32 + g * 8) * 2);
-        vis[nb] = s.seq_len - a.T + rr / a.G + 1;
+        tq[nb] = rr / a.G;
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = make_uint4(0, 0, 0, 0);
-        vis[nb] = s.seq_len;
+        tq[nb] = a.T - 1;  // padding column: any valid row, discarded
       }
+      tw[nb] = MASKED && a.tree ? a.tree[(int64_t)s.b * a.T + tq[nb]] : 0u;
     }
 
     const char* kb = a.k + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
@@ -210,7 +214,11 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 
       // ---- scale, mask, online softmax (one query row per lane column)
       const int tok0 = ti * TILE;
-      const bool edge = tok0 + TILE > s.seq_len - a.T + 1;
+      const int new0 = s.seq_len - a.T;
+      // tiles wholly inside [new0 + 1 (new0 with a tree), seq_len - window)
+      // are visible to every query
+      const bool edge = tok0 + TILE > (MASKED && a.tree ? new0 : new0 + 1) ||
+                        (MASKED && a.window > 0 && tok0 < s.seq_len - a.window);
       uint4 phi[NB], plo[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -220,7 +228,9 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float v = st[mb][nb][i] * a.scale_log2;
-            if (edge && tok0 + mb * 16 + 4 * g + i >= vis[nb]) v = -__builtin_inff();
+            const int tok = tok0 + mb * 16 + 4 * g + i;
+            if (edge && !(MASKED ? key_visible(a, tok, new0, tq[nb], tw[nb]) : tok <= new0 + tq[nb]))
+              v = -__builtin_inff();
             p[mb][i] = v;
           }
         float mt = p[0][0];
@@ -318,32 +328,46 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- launch
 
-template <bool BF, int H, int NB, bool PAGED>
+template <bool BF, int H, int NB, bool PAGED, bool MASKED>
 static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
   const size_t shmem = (size_t)(2 * a.B + 1) * sizeof(int32_t);
   // one worker per workgroup
-  hipLaunchKernelGGL((attn_mfma_kernel<BF, H, NB, PAGED>), dim3(a.W), dim3(THREADS), shmem, stream, a);
+  hipLaunchKernelGGL((attn_mfma_kernel<BF, H, NB, PAGED, MASKED>), dim3(a.W), dim3(THREADS), shmem,
+                     stream, a);
   return hipGetLastError();
 }
 
-template <bool BF, int H, bool PAGED>
+template <bool BF, int H, bool PAGED, bool MASKED>
 static hipError_t launch_mfma_nb(const AttnArgs& a, hipStream_t stream) {
   switch (a.RMAX / 16) {
-    case 1: return launch_mfma_t<BF, H, 1, PAGED>(a, stream);
-    case 2: return launch_mfma_t<BF, H, 2, PAGED>(a, stream);
-    case 3: return launch_mfma_t<BF, H, 3, PAGED>(a, stream);
-    case 4: return launch_mfma_t<BF, H, 4, PAGED>(a, stream);
+    case 1: return launch_mfma_t<BF, H, 1, PAGED, MASKED>(a, stream);
+    case 2: return launch_mfma_t<BF, H, 2, PAGED, MASKED>(a, stream);
+    case 3: return launch_mfma_t<BF, H, 3, PAGED, MASKED>(a, stream);
+    case 4: return launch_mfma_t<BF, H, 4, PAGED, MASKED>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_attn_mfma(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {
+template <bool MASKED>
+static hipError_t launch_mfma_m(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {
   if (bf16) {
-    if (H == 64) return paged ? launch_mfma_nb<true, 64, true>(a, stream) : launch_mfma_nb<true, 64, false>(a, stream);
-    return paged ? launch_mfma_nb<true, 128, true>(a, stream) : launch_mfma_nb<true, 128, false>(a, stream);
+    if (H == 64)
+      return paged ? launch_mfma_nb<true, 64, true, MASKED>(a, stream)
+                   : launch_mfma_nb<true, 64, false, MASKED>(a, stream);
+    return paged ? launch_mfma_nb<true, 128, true, MASKED>(a, stream)
+                 : launch_mfma_nb<true, 128, false, MASKED>(a, stream);
   }
-  if (H == 64) return paged ? launch_mfma_nb<false, 64, true>(a, stream) : launch_mfma_nb<false, 64, false>(a, stream);
-  return paged ? launch_mfma_nb<false, 128, true>(a, stream) : launch_mfma_nb<false, 128, false>(a, stream);
+  if (H == 64)
+    return paged ? launch_mfma_nb<false, 64, true, MASKED>(a, stream)
+                 : launch_mfma_nb<false, 64, false, MASKED>(a, stream);
+  return paged ? launch_mfma_nb<false, 128, true, MASKED>(a, stream)
+               : launch_mfma_nb<false, 128, false, MASKED>(a, stream);
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {
+  const bool masked = a.window > 0 || a.tree != nullptr;
+  return masked ? launch_mfma_m<true>(a, bf16, H, paged, stream)
+                : launch_mfma_m<false>(a, bf16, H, paged, stream);
 }
 
 }  // namespace kvc

@@ -35,7 +35,9 @@
 
 namespace kvc {
 
-template <bool BF, int H, int R, int LPR, bool PAGED, int WPE>
+// MASKED: a window or draft-tree mask is in use (the general per-key test);
+// otherwise the causal test alone, which keeps the loop leaner.
+template <bool BF, int H, int R, int LPR, bool PAGED, int WPE, bool MASKED>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_valu_kernel(AttnArgs a) {
   constexpr int DPL = H / LPR;         // dims per lane: 8 or 16
   constexpr int NCH = DPL / 8;         // 16-byte chunks per lane per row
@@ -122,9 +124,16 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
   while (true) {
     const bool has_next = x_next < part.hi;
     const Segment nxt = has_next ? find_segment(a, s_pre, part, x_next) : cur;
-    // Row r = t * G + g sees keys j < seq_len - T + t + 1; only tiles that
-    // reach past vis_min need the mask.
-    const int vis_min = cur.seq_len - a.T + 1;
+    // Row r = t * G + g is new token t. Tiles wholly inside [mask_lo,
+    // mask_hi) are visible to every row; others take the per-key test
+    // (causal or tree rule among the new rows, window at the start).
+    const int new0 = cur.seq_len - a.T;
+    const int mask_hi = MASKED && a.tree ? new0 : new0 + 1;
+    const int mask_lo = MASKED && a.window > 0 ? cur.seq_len - a.window : INT_MIN;
+    uint32_t tword[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      tword[r] = MASKED && a.tree ? a.tree[(int64_t)cur.b * a.T + r / a.G] : 0u;
 
     float m[R], l[R], o[R][DPL];
 #pragma unroll
@@ -172,15 +181,18 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
         for (int r = 0; r < R; ++r) sc[r][i] = group_sum<LPR>(sc[r][i]) * a.scale_log2;
 
-      // ---- causal / length mask (only the last tiles of a sequence)
+      // ---- mask (only a unit's first and last tiles)
       const int tok0 = ti * TILE;
-      if (tok0 + TILE > vis_min) {
+      if (tok0 + TILE > mask_hi || tok0 < mask_lo) {
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {
           const int tok = tok0 + grp + GROUPS * i;
 #pragma unroll
-          for (int r = 0; r < R; ++r)
-            if (tok >= vis_min + r / a.G) sc[r][i] = -__builtin_inff();
+          for (int r = 0; r < R; ++r) {
+            const bool ok = MASKED ? key_visible(a, tok, new0, r / a.G, tword[r])
+                                   : tok <= new0 + r / a.G;
+            if (!ok) sc[r][i] = -__builtin_inff();
+          }
         }
       }
 
@@ -284,7 +296,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
 
 // ---------------------------------------------------------------- launch
 
-template <bool BF, int H, int R, bool PAGED>
+template <bool BF, int H, int R, bool PAGED, bool MASKED>
 static hipError_t launch_valu_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int LPR = 8;
   // Two waves per SIMD (at most 256 registers per lane) wherever the loop
@@ -293,39 +305,52 @@ static hipError_t launch_valu_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int WPE = (H == 128 && R <= 4) || H == 64 ? 2 : 1;
   const size_t shmem = (size_t)(2 * a.B + 1) * sizeof(int32_t);
   // one worker per workgroup; its waves interleave the tiles
-  hipLaunchKernelGGL((attn_valu_kernel<BF, H, R, LPR, PAGED, WPE>), dim3(a.W), dim3(THREADS),
+  hipLaunchKernelGGL((attn_valu_kernel<BF, H, R, LPR, PAGED, WPE, MASKED>), dim3(a.W), dim3(THREADS),
                      shmem, stream, a);
   return hipGetLastError();
 }
 
-template <bool BF, int H, bool PAGED>
+template <bool BF, int H, bool PAGED, bool MASKED>
 static hipError_t launch_valu_r(const AttnArgs& a, hipStream_t stream) {
   switch (a.R) {
-    case 1: return launch_valu_t<BF, H, 1, PAGED>(a, stream);
-    case 2: return launch_valu_t<BF, H, 2, PAGED>(a, stream);
-    case 3: return launch_valu_t<BF, H, 3, PAGED>(a, stream);
-    case 4: return launch_valu_t<BF, H, 4, PAGED>(a, stream);
+    case 1: return launch_valu_t<BF, H, 1, PAGED, MASKED>(a, stream);
+    case 2: return launch_valu_t<BF, H, 2, PAGED, MASKED>(a, stream);
+    case 3: return launch_valu_t<BF, H, 3, PAGED, MASKED>(a, stream);
+    case 4: return launch_valu_t<BF, H, 4, PAGED, MASKED>(a, stream);
     default: break;
   }
   if constexpr (H == 64) {
     switch (a.R) {
-      case 5: return launch_valu_t<BF, H, 5, PAGED>(a, stream);
-      case 6: return launch_valu_t<BF, H, 6, PAGED>(a, stream);
-      case 7: return launch_valu_t<BF, H, 7, PAGED>(a, stream);
-      case 8: return launch_valu_t<BF, H, 8, PAGED>(a, stream);
+      case 5: return launch_valu_t<BF, H, 5, PAGED, MASKED>(a, stream);
+      case 6: return launch_valu_t<BF, H, 6, PAGED, MASKED>(a, stream);
+      case 7: return launch_valu_t<BF, H, 7, PAGED, MASKED>(a, stream);
+      case 8: return launch_valu_t<BF, H, 8, PAGED, MASKED>(a, stream);
       default: break;
     }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_valu(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {
+template <bool MASKED>
+static hipError_t launch_valu_m(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {
   if (bf16) {
-    if (H == 64) return paged ? launch_valu_r<true, 64, true>(a, stream) : launch_valu_r<true, 64, false>(a, stream);
-    return paged ? launch_valu_r<true, 128, true>(a, stream) : launch_valu_r<true, 128, false>(a, stream);
+    if (H == 64)
+      return paged ? launch_valu_r<true, 64, true, MASKED>(a, stream)
+                   : launch_valu_r<true, 64, false, MASKED>(a, stream);
+    return paged ? launch_valu_r<true, 128, true, MASKED>(a, stream)
+                 : launch_valu_r<true, 128, false, MASKED>(a, stream);
   }
-  if (H == 64) return paged ? launch_valu_r<false, 64, true>(a, stream) : launch_valu_r<false, 64, false>(a, stream);
-  return paged ? launch_valu_r<false, 128, true>(a, stream) : launch_valu_r<false, 128, false>(a, stream);
+  if (H == 64)
+    return paged ? launch_valu_r<false, 64, true, MASKED>(a, stream)
+                 : launch_valu_r<false, 64, false, MASKED>(a, stream);
+  return paged ? launch_valu_r<false, 128, true, MASKED>(a, stream)
+               : launch_valu_r<false, 128, false, MASKED>(a, stream);
+}
+
+hipError_t launch_attn_valu(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {
+  const bool masked = a.window > 0 || a.tree != nullptr;
+  return masked ? launch_valu_m<true>(a, bf16, H, paged, stream)
+                : launch_valu_m<false>(a, bf16, H, paged, stream);
 }
 
 }  // namespace kvc

@@ -75,6 +75,11 @@ struct AttnArgs {
   const char* v_new;
   char* k_store;  // the K and V caches again, writable
   char* v_store;
+  // Visibility options (both off by default): a sliding window of `window`
+  // positions (0: none), and per (b, t) a mask word over the T new rows
+  // (nullptr: causal inside the block). See unit_first_step and key_visible.
+  int32_t window;
+  const uint32_t* tree;  // [B, T]
 };
 
 // ---------------------------------------------------------------- dtypes
@@ -213,6 +218,36 @@ __device__ __forceinline__ bool seq_valid(int32_t len, int32_t T, int32_t capaci
   return len >= T && len <= capacity;
 }
 
+// First 128-token step of a sequence of length len that holds a visible
+// key: with a window of W positions the earliest key any of the T new
+// tokens sees is len - T - W + 1 (for t = 0); without one it is 0.
+__device__ __forceinline__ int unit_first_step(const AttnArgs& a, int len) {
+  return a.window > 0 ? max(0, len - a.T - a.window + 1) / STEP : 0;
+}
+
+// Steps a unit of a sequence of length len streams (0 for invalid lengths).
+__device__ __forceinline__ int unit_steps(const AttnArgs& a, int len) {
+  return seq_valid(len, a.T, a.capacity) ? (len + STEP - 1) / STEP - unit_first_step(a, len) : 0;
+}
+
+// Whether key position tok is visible to new token t of a sequence whose new
+// rows start at new0 (= seq_len - T), given that token's tree word (ignored
+// without a tree mask). Prior rows are visible, new rows by the causal rule
+// or the tree word, rows past the sequence never; a window further requires
+// tok > new0 + t - W.
+__device__ __forceinline__ bool key_visible(const AttnArgs& a, int tok, int new0, int t,
+                                            uint32_t word) {
+  bool ok;
+  if (tok < new0)
+    ok = true;
+  else if (a.tree)
+    ok = tok - new0 < a.T && ((word >> (tok - new0)) & 1u);
+  else
+    ok = tok <= new0 + t;
+  if (a.window > 0) ok = ok && tok > new0 + t - a.window;
+  return ok;
+}
+
 // s_pre[0..B]: exclusive prefix sums of steps per sequence (0 for invalid
 // lengths); s_pre[B + 1 + b]: the length of sequence b, so that later reads
 // of it are LDS reads rather than global loads (a global load inside the
@@ -227,8 +262,7 @@ __device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_
   for (int i = 0; i < per; ++i) {
     int b = b0 + i;
     if (b < a.B) {
-      int32_t len = a.seq_lens[b];
-      local += seq_valid(len, a.T, a.capacity) ? (len + STEP - 1) / STEP : 0;
+      local += unit_steps(a, a.seq_lens[b]);
     }
   }
   // inclusive scan of `local` over the workgroup
@@ -250,7 +284,7 @@ __device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_
       s_pre[b] = run;
       int32_t len = a.seq_lens[b];
       s_pre[a.B + 1 + b] = len;
-      run += seq_valid(len, a.T, a.capacity) ? (len + STEP - 1) / STEP : 0;
+      run += unit_steps(a, len);
     }
   }
   if (tid == THREADS - 1) s_pre[a.B] = carry + incl;
@@ -265,7 +299,7 @@ struct Segment {
   int rb;         // query-row block
   int unit;       // (b * K + k) * RB + rb
   int seq_len;    // valid tokens
-  int t_begin;    // first step of this segment (within the unit)
+  int t_begin;    // first step of this segment (counted from the sequence's first token)
   int t_end;      // one past the last step
   int n_parts;    // workers sharing the unit (1: this one writes the output directly)
   int first_wg;   // first worker sharing the unit
@@ -324,6 +358,10 @@ __device__ __forceinline__ Segment find_segment(const AttnArgs& a, const int32_t
   const int64_t ustart = x - s.t_begin;
   s.first_wg = p.owner(ustart);
   s.n_parts = p.owner(ustart + tb - 1) - s.first_wg + 1;
+  // step indices from here on count from the sequence's first token
+  const int fs = unit_first_step(a, s.seq_len);
+  s.t_begin += fs;
+  s.t_end += fs;
   return s;
 }
 

@@ -34,6 +34,8 @@ class Run:
     lse: torch.Tensor | None
     scale: float
     table: np.ndarray | None = None
+    window: int = 0
+    tree: list | None = None  # per sequence, T mask words
 
 
 def build_cache(inp, layout, seed, block_size=16, extra_blocks=3, capacity=None, pad=float("nan")):
@@ -48,7 +50,7 @@ def build_cache(inp, layout, seed, block_size=16, extra_blocks=3, capacity=None,
 
 def run_case(B, T, N, K, H, dtype, prior, layout="contiguous", seed=1, num_workgroups=0,
              out_dtype=torch.float32, block_size=16, scale=None, device="cuda", draw_device="cpu",
-             capacity=None, fused=False):
+             capacity=None, fused=False, window=0, tree=None):
     """Build the cache from the prior rows, then append the new rows and attend:
     two calls (append, then decode/verify) or, with ``fused``, one
     append_attend call."""
@@ -62,6 +64,21 @@ def run_case(B, T, N, K, H, dtype, prior, layout="contiguous", seed=1, num_workg
     seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(device)
     max_len = int(inp.seq_lens.max())
     scale = 1.0 / math.sqrt(H) if scale is None else scale
+    if window or tree is not None:
+        q = inp.q[:, 0].contiguous() if T == 1 else inp.q
+        tm = None
+        if tree is not None:
+            tm = torch.tensor(np.asarray(tree, dtype=np.uint32).view(np.int32), device=device)
+        kw = dict(k_new=inp.k_new, v_new=inp.v_new) if fused else {}
+        if not fused:
+            kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+        out, lse = kvc.attend(q, cache, seq_lens, max_len, window=window, tree_mask=tm, scale=scale,
+                              out_dtype=out_dtype, num_workgroups=num_workgroups, return_lse=True,
+                              **kw)
+        if T == 1:
+            out, lse = out[:, None], lse[:, None]
+        torch.cuda.synchronize()
+        return Run(inp, cache, seq_lens, out, lse, scale, table, window, tree)
     if fused:
         q = inp.q[:, 0].contiguous() if T == 1 else inp.q
         out, lse = kvc.append_attend(q, inp.k_new, inp.v_new, cache, seq_lens, max_len, scale=scale,
@@ -93,14 +110,16 @@ def to_device(inp, device):
     return out
 
 
-def oracle_unit(inp, b, k, scale):
-    """Oracle output [T, G, H] and lse [T, G] of sequence b, key-value head k."""
+def oracle_unit(inp, b, k, scale, window=0, tree=None):
+    """Oracle output [T, G, H] and lse [T, G] of sequence b, key-value head k
+    (optionally with a window and the sequence's tree words)."""
     G = inp.N // inp.K
     kb, vb = logical_kv(inp, b)
     kk = kb[:, k : k + 1, :].double().cpu().numpy()
     vv = vb[:, k : k + 1, :].double().cpu().numpy()
     q = inp.q[b : b + 1, :, k * G : (k + 1) * G, :].double().cpu().numpy()
-    o, l = attend(q, [kk], [vv], scale)
+    o, l = attend(q, [kk], [vv], scale, window=window,
+                  tree_words=None if tree is None else [tree[b]])
     return o[0], l[0]
 
 
@@ -110,7 +129,7 @@ def compare_units(run, units, out_tol=TOL, lse_tol=TOL):
     G = inp.N // inp.K
     worst_o = worst_l = 0.0
     for b, k in units:
-        o_ref, l_ref = oracle_unit(inp, b, k, run.scale)
+        o_ref, l_ref = oracle_unit(inp, b, k, run.scale, run.window, run.tree)
         o = run.out[b, :, k * G : (k + 1) * G, :].double().cpu().numpy()
         l = run.lse[b, :, k * G : (k + 1) * G].double().cpu().numpy()
         assert np.all(np.isfinite(o)), f"non-finite output in unit {(b, k)}"

@@ -175,3 +175,27 @@ def test_append_attend_host_errors(lib):
     # an empty batch is a successful no-op, with or without buffers
     assert aa(B=0) == E.KVC_OK
     assert aa(B=0, kn=None, vn=None, q=None) == E.KVC_OK
+
+
+def test_attn_options_layout_and_errors(lib):
+    E = _lib
+    assert ctypes.sizeof(_lib.KvcAttnOptions) == 32  # 3 pointers, 2 int32
+    c = _cache()
+
+    def at(window=0, reserved=0, tree=None, opts=True, **kw):
+        o = _lib.KvcAttnOptions()
+        o.window = window
+        o.reserved = reserved
+        o.tree_mask = tree
+        return lib.kvc_attn(ctypes.byref(c), ctypes.byref(o) if opts else None, FAKE, FAKE,
+                            E.KVC_F32, None, kw.get("B", 8), kw.get("T", 5), 64, 8, 128, FAKE,
+                            4096, 0.1, 0, kw.get("ws", FAKE), 1 << 30, None)
+
+    assert at(window=-1) == E.KVC_ERR_INVALID
+    assert at(reserved=3) == E.KVC_ERR_INVALID
+    assert at(tree=FAKE + 2) == E.KVC_ERR_INVALID
+    assert at(T=17) == E.KVC_ERR_INVALID
+    assert at(ws=None) == E.KVC_ERR_WORKSPACE
+    assert at(B=0) == E.KVC_OK
+    assert at(B=0, opts=False) == E.KVC_OK
+    assert at(B=0, window=7, tree=FAKE) == E.KVC_OK

@@ -381,3 +381,81 @@ def test_graph_replays_match_eager(gpu_device):
             assert torch.equal(other, eager_attend)
         results.append(float(out_g.abs().max()))
     say(f"  graph replays ok, max|out| {results}")
+
+
+# ----------------------------------------------------------------- window and draft-tree options
+
+
+def _random_tree_words(rng, B, T):
+    """Per sequence, the mask words of a random draft tree (each draft's
+    parent is an earlier draft or none)."""
+    from oracle import ancestor_words
+
+    words = []
+    for _ in range(B):
+        parents = [-1] + [int(rng.integers(-1, u)) for u in range(1, T)]
+        words.append(ancestor_words(parents))
+    return words
+
+
+WINDOW_CASES = [SMALL[0], SMALL[3], SMALL[4], SMALL[7], SMALL[9], SMALL[11], SMALL[13]]
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("W", [1, 5, 40, 129, 300])
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=_ids(WINDOW_CASES))
+def test_sliding_window_matches_oracle(gpu_device, case, W, layout):
+    B, T, N, K, H, dtype, prior = case
+    run = run_case(B, T, N, K, H, dtype, prior, layout=layout, seed=400 + W, window=W)
+    compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("case", [SMALL[3], SMALL[9]], ids=_ids([SMALL[3], SMALL[9]]))
+def test_window_not_shorter_than_the_sequence_is_the_plain_call(gpu_device, case):
+    B, T, N, K, H, dtype, prior = case
+    kw = dict(seed=410, num_workgroups=23)
+    plain = run_case(B, T, N, K, H, dtype, prior, **kw)
+    wide = run_case(B, T, N, K, H, dtype, prior, window=max(prior) + T, **kw)
+    assert torch.equal(plain.out, wide.out) and torch.equal(plain.lse, wide.lse)
+
+
+@pytest.mark.parametrize("nwg", [0, 3, 5000])
+def test_window_with_any_workgroup_count(gpu_device, nwg):
+    for T, N, K in [(1, 32, 8), (5, 64, 8)]:
+        run = run_case(3, T, N, K, 128, BF, [700, 65, 2000], seed=411, num_workgroups=nwg, window=333)
+        compare_units(run, all_units(run.inp))
+
+
+TREE_CASES = [SMALL[7], SMALL[8], SMALL[9], SMALL[10], SMALL[11], SMALL[12], SMALL[13]]
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("case", TREE_CASES, ids=_ids(TREE_CASES))
+def test_draft_tree_mask_matches_oracle(gpu_device, case, layout):
+    B, T, N, K, H, dtype, prior = case
+    rng = np.random.default_rng(500 + T)
+    words = _random_tree_words(rng, B, T)
+    run = run_case(B, T, N, K, H, dtype, prior, layout=layout, seed=501 + T, tree=words)
+    compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("case", [SMALL[7], SMALL[9], SMALL[12]], ids=_ids([SMALL[7], SMALL[9], SMALL[12]]))
+def test_causal_tree_words_are_the_plain_verify(gpu_device, case):
+    from oracle import causal_tree_words
+
+    B, T, N, K, H, dtype, prior = case
+    kw = dict(seed=510, num_workgroups=17)
+    plain = run_case(B, T, N, K, H, dtype, prior, **kw)
+    tree = run_case(B, T, N, K, H, dtype, prior, tree=[causal_tree_words(T)] * B, **kw)
+    assert torch.equal(plain.out, tree.out) and torch.equal(plain.lse, tree.lse)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("T,N,K,H", [(4, 16, 4, 64), (6, 64, 8, 128), (16, 8, 2, 64)])
+def test_window_and_tree_together(gpu_device, T, N, K, H, fused):
+    B = 3
+    rng = np.random.default_rng(520 + T)
+    words = _random_tree_words(rng, B, T)
+    run = run_case(B, T, N, K, H, BF, [90, 0, 700], seed=521 + T, tree=words, window=50,
+                   fused=fused)
+    compare_units(run, all_units(run.inp))
