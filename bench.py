@@ -110,16 +110,34 @@ class Step:
         self.nwg = nwg
         need = kvc.workspace_bytes(w.B, w.T, w.N, w.K, w.H, self.max_len, nwg)
         self.ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        # options: a sliding window and / or a draft-tree mask among the new tokens
+        self.opts = bool(w.window or w.tree_parents)
+        self.tree = None
+        if w.tree_parents:
+            from workloads import tree_mask_words
+
+            words = tree_mask_words(w.tree_parents).view(np.int32)
+            self.tree = torch.from_numpy(np.tile(words, (w.B, 1))).to(dev)
 
     def append(self):
         self.kvc.append(self.cache, self.inp.k_new, self.inp.v_new, self.seq_lens)
 
     def append_attend(self):
+        if self.opts:
+            self.kvc.attend(self.q, self.cache, self.seq_lens, self.max_len, window=self.w.window,
+                            tree_mask=self.tree, k_new=self.inp.k_new, v_new=self.inp.v_new,
+                            out=self.out, out_dtype=self.w.dtype, num_workgroups=self.nwg, ws=self.ws)
+            return
         self.kvc.append_attend(self.q, self.inp.k_new, self.inp.v_new, self.cache, self.seq_lens,
                                self.max_len, out=self.out, out_dtype=self.w.dtype,
                                num_workgroups=self.nwg, ws=self.ws)
 
     def attend(self):
+        if self.opts:
+            self.kvc.attend(self.q, self.cache, self.seq_lens, self.max_len, window=self.w.window,
+                            tree_mask=self.tree, out=self.out, out_dtype=self.w.dtype,
+                            num_workgroups=self.nwg, ws=self.ws)
+            return
         f = self.kvc.decode if self.w.T == 1 else self.kvc.verify
         f(self.q, self.cache, self.seq_lens, self.max_len, out=self.out, out_dtype=self.w.dtype,
           num_workgroups=self.nwg, ws=self.ws)
@@ -156,7 +174,12 @@ def profiled_traffic(kernel: str, workload: str):
 
 
 def kv_bytes(w, seq_lens) -> int:
-    return int(np.sum(seq_lens)) * 2 * w.K * w.H * w.elem_bytes
+    """Algorithmic K and V bytes of one step: every key and value row some
+    new token sees, once (with a window W: the last W + T - 1 positions)."""
+    rows = np.asarray(seq_lens, dtype=np.int64)
+    if w.window:
+        rows = np.minimum(rows, w.window + w.T - 1)
+    return int(np.sum(rows)) * 2 * w.K * w.H * w.elem_bytes
 
 
 def cpu_baseline(w, prior, seed, budget_s):
@@ -164,7 +187,7 @@ def cpu_baseline(w, prior, seed, budget_s):
     same workload until ``budget_s`` seconds pass; report KV GB/s."""
     import torch
 
-    from oracle import attend
+    from oracle import ancestor_words, attend
     from workloads import draw_inputs, logical_kv
 
     try:
@@ -175,6 +198,7 @@ def cpu_baseline(w, prior, seed, budget_s):
         blas_threads = 1
     scale = 1.0 / math.sqrt(w.H)
     G = w.N // w.K
+    tree = [ancestor_words(list(w.tree_parents))] if w.tree_parents else None
     done_bytes = 0
     units = 0
     elapsed = 0.0
@@ -189,9 +213,10 @@ def cpu_baseline(w, prior, seed, budget_s):
             vv = vb[:, k : k + 1].double().numpy()
             q = one.q[:, :, k * G : (k + 1) * G].double().numpy()
             t0 = time.perf_counter()
-            attend(q, [kk], [vv], scale)
+            attend(q, [kk], [vv], scale, window=w.window, tree_words=tree)
             elapsed += time.perf_counter() - t0
-            done_bytes += kk.shape[0] * 2 * w.H * w.elem_bytes
+            rows = min(kk.shape[0], w.window + w.T - 1) if w.window else kk.shape[0]
+            done_bytes += rows * 2 * w.H * w.elem_bytes
             units += 1
             if elapsed >= budget_s:
                 break

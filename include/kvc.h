@@ -205,9 +205,13 @@ kvc_status kvc_append_attend(const kvc_cache *cache, const void *k_new, const vo
  *   lectures 10 and 12", section "Reducing the KV cache": a token looks only
  *   at the most recent tokens; "Stanford CS336 Day 13 - Inference", section
  *   "Local Attention"): new token t, at position i = seq_lens[b] - T + t,
- *   sees only keys at positions i - W + 1 .. i. Only the keys some query of
- *   the call can see are read, so a call streams at most W + T - 1 (rounded
- *   out to 128-token steps) positions per sequence and head.
+ *   sees only keys at positions i - W + 1 .. i. Only keys at positions
+ *   >= seq_lens[b] - T - W + 1 are ever read (at most W + T - 1 positions per
+ *   sequence and head), so with a block table the entries of blocks wholly
+ *   before that position are not read and those blocks may be unmapped or
+ *   reused: the cache a windowed call needs does not grow with the sequence
+ *   ("Stanford CS336 Day 13 - Inference", "Local Attention": rows that left
+ *   the window can leave the cache).
  * tree_mask: NULL for the causal rule inside the block, or device
  *   [B, T] uint32 words for draft-tree verification ("Accelerating Sonar
  *   through speculation", section "EAGLE": tree-shaped drafts are verified

@@ -147,8 +147,10 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
     const int32_t* trow = PAGED ? a.table + (int64_t)s.b * a.max_blocks : nullptr;
     const int bmask = (1 << a.block_shift) - 1;
     bool bad = false;
+    const int vis0 = MASKED ? first_visible(a, s.seq_len) : 0;
     auto row_off = [&](int tok) -> int64_t {
       tok = min(tok, s.seq_len - 1);
+      if constexpr (MASKED) tok = max(tok, vis0);
       if constexpr (PAGED) {
         int blk = trow[tok >> a.block_shift];
         if ((unsigned)blk >= (unsigned)a.num_blocks) {

@@ -72,9 +72,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
     return a.v + (int64_t)g.k * a.stride_head + (PAGED ? 0 : (int64_t)g.b * a.stride_seq);
   };
   // Byte offset of token `tok` of sequence g.b (clamped to its last valid
-  // row); an out-of-range block entry reads block 0 and flags the unit.
+  // row, and under a window to its first visible one); an out-of-range block
+  // entry reads block 0 and flags the unit.
   auto row_off = [&](const Segment& g, int tok, bool& bad) -> int64_t {
     tok = min(tok, g.seq_len - 1);
+    if constexpr (MASKED) tok = max(tok, first_visible(a, g.seq_len));
     if constexpr (PAGED) {
       int blk = a.table[(int64_t)g.b * a.max_blocks + (tok >> a.block_shift)];
       if ((unsigned)blk >= (unsigned)a.num_blocks) {

@@ -230,6 +230,14 @@ __device__ __forceinline__ int unit_steps(const AttnArgs& a, int len) {
   return seq_valid(len, a.T, a.capacity) ? (len + STEP - 1) / STEP - unit_first_step(a, len) : 0;
 }
 
+// First key position a unit's queries can see (0 without a window). Rows
+// before it are never read, so with a block table the blocks wholly before
+// it need not be mapped: under a window the cache a call touches no longer
+// grows with the sequence.
+__device__ __forceinline__ int first_visible(const AttnArgs& a, int len) {
+  return a.window > 0 ? max(0, len - a.T - a.window + 1) : 0;
+}
+
 // Whether key position tok is visible to new token t of a sequence whose new
 // rows start at new0 (= seq_len - T), given that token's tree word (ignored
 // without a tree mask). Prior rows are visible, new rows by the causal rule

@@ -459,3 +459,40 @@ def test_window_and_tree_together(gpu_device, T, N, K, H, fused):
     run = run_case(B, T, N, K, H, BF, [90, 0, 700], seed=521 + T, tree=words, window=50,
                    fused=fused)
     compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("T,N,K,H", [(1, 32, 8, 128), (5, 64, 8, 128), (3, 8, 2, 64)])
+def test_window_never_reads_blocks_before_it(gpu_device, T, N, K, H):
+    """Paged cache whose blocks wholly before the first visible position are
+    unmapped (table entry -1) and whose pool is NaN everywhere they would
+    point: outputs stay finite and match the oracle, so no row or table
+    entry before the window was read."""
+    from workloads import layout_paged, make_block_table
+
+    B, W, bs = 3, 100, 16
+    inp = draw_inputs(B, T, N, K, H, BF, np.array([1000, 77, 513]), 530 + T, device="cpu")
+    dev = gpu_device
+    for name in ("q", "k_new", "v_new", "ctx_k", "ctx_v"):
+        setattr(inp, name, getattr(inp, name).to(dev))
+    table, nb = make_block_table(531, inp.seq_lens, bs, extra_blocks=2)
+    pk, pv = layout_paged(inp, table, nb, bs, pad_value=float("nan"))
+    cut = table.copy()
+    for b in range(B):
+        first = max(0, int(inp.seq_lens[b]) - T - W + 1)
+        for blk in range(first // bs):
+            pk[cut[b, blk]] = float("nan")
+            pv[cut[b, blk]] = float("nan")
+            cut[b, blk] = -1
+    cache = kvc.Cache(pk, pv, torch.from_numpy(cut).to(dev))
+    seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(dev)
+    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+    L = int(inp.seq_lens.max())
+    q = inp.q[:, 0].contiguous() if T == 1 else inp.q
+    out, lse = kvc.attend(q, cache, seq_lens, L, window=W, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    if T == 1:
+        out, lse = out[:, None], lse[:, None]
+    from gpu_cases import Run
+
+    run = Run(inp, cache, seq_lens, out, lse, 1 / math.sqrt(H), window=W)
+    compare_units(run, all_units(inp))

@@ -96,3 +96,26 @@ def test_paged_long_b8_sampled(gpu_device):
     units = [(b, (3 * b + 1) % w.K) for b in range(w.B)]
     compare_units(run, units)
     assert torch.isfinite(run.out).all()
+
+
+def test_sliding_window_b32_sampled(gpu_device):
+    w = WORKLOADS["sliding_window_b32"]
+    run = run_case(w.B, w.T, w.N, w.K, w.H, w.dtype, _prior(w), layout=w.layout, seed=w.seed,
+                   draw_device=gpu_device, window=w.window)
+    rng = np.random.default_rng(w.seed)
+    units = [(int(b), int(rng.integers(0, w.K))) for b in rng.permutation(w.B)[:12]]
+    compare_units(run, units)
+    assert torch.isfinite(run.out).all()
+
+
+def test_tree_verify_b32_t8_sampled(gpu_device):
+    from workloads import tree_mask_words
+
+    w = WORKLOADS["tree_verify_b32_t8"]
+    words = [list(tree_mask_words(w.tree_parents))] * w.B
+    run = run_case(w.B, w.T, w.N, w.K, w.H, w.dtype, _prior(w), layout=w.layout, seed=w.seed,
+                   draw_device=gpu_device, tree=words)
+    rng = np.random.default_rng(w.seed)
+    units = [(int(b), int(rng.integers(0, w.K))) for b in rng.permutation(w.B)[:24]]
+    compare_units(run, units)
+    assert torch.isfinite(run.out).all()

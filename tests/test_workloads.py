@@ -84,3 +84,18 @@ def test_workload_shapes(name):
     w = WORKLOADS[name]
     assert w.N % w.K == 0 and w.H in (64, 128) and 1 <= w.T <= 16
     assert w.dtype in (torch.float16, torch.bfloat16)
+    assert w.window >= 0
+    if w.tree_parents:
+        assert len(w.tree_parents) == w.T and w.tree_parents[0] == -1
+        assert all(-1 <= p < u for u, p in enumerate(w.tree_parents))
+
+
+def test_tree_mask_words_agree_with_the_oracle_reading():
+    """The input generator's words and the oracle's are written separately;
+    they must agree on chains, stars and the measured tree."""
+    from oracle import ancestor_words
+    from workloads import tree_mask_words
+
+    for parents in ([-1], [-1, 0, 1, 2], [-1, 0, 0, 0, 0], [-1, 0, 0, 1, 1, 2, 2, 3], [-1, -1, 1, 0],
+                    WORKLOADS["tree_verify_b32_t8"].tree_parents):
+        assert [int(x) for x in tree_mask_words(list(parents))] == ancestor_words(list(parents))

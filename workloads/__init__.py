@@ -15,6 +15,7 @@ from .synth import (
     layout_paged,
     logical_kv,
     make_block_table,
+    tree_mask_words,
 )
 
 __all__ = [
@@ -28,4 +29,5 @@ __all__ = [
     "layout_paged",
     "logical_kv",
     "make_block_table",
+    "tree_mask_words",
 ]

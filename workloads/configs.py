@@ -1,4 +1,4 @@
-"""The five synthetic workloads, named by what they are.
+"""The synthetic workloads, named by what they are.
 
 Shapes follow the pages on KV-cached inference:
 
@@ -12,7 +12,15 @@ Shapes follow the pages on KV-cached inference:
   "Speculative decoding": n drafted tokens scored in one target pass) with
   4 drafts, i.e. T = 5 query tokens;
 * 16-token blocks and a per-sequence block table from "CS336, lectures 10 and
-  12: inference and evaluation", section "PagedAttention".
+  12: inference and evaluation", section "PagedAttention";
+* local attention with a 4096-token window over long contexts ("CS336,
+  lectures 10 and 12", section "Reducing the KV cache", which names Mistral
+  7B among the local-attention models; 4096 is Mistral 7B's published
+  window, a reading, as the pages give no number);
+* a draft tree of 8 tokens verified in one pass ("Accelerating Sonar through
+  speculation", section "EAGLE": top-k branches at each node; the shape
+  here, a root with two children and two grandchildren each plus one more
+  level, is a reading).
 
 "Context" in each description is the PRIOR cached context P_b; the T new
 tokens are appended on top of it, so a sequence attends over P_b + T keys.
@@ -44,6 +52,8 @@ class Workload:
     layers: int = 1
     block_size: int = 16
     prior_sweep: tuple = field(default_factory=tuple)
+    window: int = 0  # sliding window (0: full context)
+    tree_parents: tuple = ()  # draft tree among the T new tokens (empty: causal)
 
     @property
     def G(self) -> int:
@@ -92,6 +102,21 @@ WORKLOADS = {
                     "16-token blocks scattered by a seeded permutation",
         B=8, N=32, K=8, H=128, T=1, dtype=torch.bfloat16,
         prior_lo=32768, prior_hi=131072, layout="paged", seed=SEED_BASE + 5,
+    ),
+    "sliding_window_b32": Workload(
+        name="sliding_window_b32",
+        description="B=32, N=32, K=8, H=128, bf16, T=1, cached context U[8192,32768], "
+                    "sliding window of 4096 positions, contiguous",
+        B=32, N=32, K=8, H=128, T=1, dtype=torch.bfloat16,
+        prior_lo=8192, prior_hi=32768, layout="contiguous", seed=SEED_BASE + 6, window=4096,
+    ),
+    "tree_verify_b32_t8": Workload(
+        name="tree_verify_b32_t8",
+        description="B=32, N=64, K=8, H=128, bf16, T=8 draft-tree tokens (parents "
+                    "-1,0,0,1,1,2,2,3), cached context U[2048,8192], contiguous",
+        B=32, N=64, K=8, H=128, T=8, dtype=torch.bfloat16,
+        prior_lo=2048, prior_hi=8192, layout="contiguous", seed=SEED_BASE + 7,
+        tree_parents=(-1, 0, 0, 1, 1, 2, 2, 3),
     ),
 }
 

@@ -165,3 +165,20 @@ def layout_paged(inp: Inputs, table: np.ndarray, num_blocks: int, block_size: in
         pk[blk, :, slot, :] = inp.ctx_k
         pv[blk, :, slot, :] = inp.ctx_v
     return pk, pv
+
+
+def tree_mask_words(parents) -> np.ndarray:
+    """Mask words describing a draft tree among the T new tokens, as the
+    caller hands them to the attention call: word t has bit u set when new
+    token u is t itself or one of its ancestors (parents[u] is u's parent, an
+    earlier token, or -1 for a root). uint32 [T]."""
+    T = len(parents)
+    words = np.zeros(T, dtype=np.uint32)
+    for t in range(T):
+        u = t
+        while u >= 0:
+            if parents[u] >= u:
+                raise ValueError("a parent must come before its child")
+            words[t] |= np.uint32(1 << u)
+            u = parents[u]
+    return words
