@@ -14,7 +14,8 @@
 // hold 8 tokens of one h: eight lanes load 8 token rows and swap 16-bit
 // elements with an 8 x 8 register transpose (swizzle + DPP).
 // p is split into a 16-bit high part and a 16-bit remainder, each multiplied
-// by V on the matrix cores, so p.v keeps close to fp32 precision.
+// by V on the matrix cores, so p.v keeps about 16 bits of p (within 2^-16
+// relative, far inside the 2e-3 gate).
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
@@ -35,21 +36,26 @@ __device__ __forceinline__ floatx4 mfma16(uint4 a, uint4 b, floatx4 c) {
   }
 }
 
-// 16-bit bits of a probability weight (finite, >= 0): round to nearest even
-// without the NaN path of the general conversion.
+// Two probability weights e0, e1 (finite, >= 0) as a packed 16-bit high
+// part and a packed 16-bit remainder, hi + lo = e to about 2^-16 relative.
+// bf16: the high part is e with its low 16 bits cut (exact to take away, so
+// the remainder e - hi is exact in fp32), the remainder is cut the same way;
+// each pair is packed by one byte permute. f16: round-toward-zero packs.
 template <bool BF>
-__device__ __forceinline__ uint32_t to16(float f) {
+__device__ __forceinline__ void split_pair(float e0, float e1, uint32_t& hi, uint32_t& lo) {
   if constexpr (BF) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t u0 = __float_as_uint(e0), u1 = __float_as_uint(e1);
+    // bytes 2,3 of u0 then bytes 2,3 of u1 (v_perm_b32: bytes 0-3 index S1, 4-7 S0)
+    hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+    const float r0 = e0 - __uint_as_float(u0 & 0xffff0000u);
+    const float r1 = e1 - __uint_as_float(u1 & 0xffff0000u);
+    lo = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
   } else {
-    return f32_to_f16_bits(f);
+    const auto h = __builtin_amdgcn_cvt_pkrtz(e0, e1);
+    hi = __builtin_bit_cast(uint32_t, h);
+    const auto l = __builtin_amdgcn_cvt_pkrtz(e0 - (float)h[0], e1 - (float)h[1]);
+    lo = __builtin_bit_cast(uint32_t, l);
   }
-}
-template <bool BF>
-__device__ __forceinline__ float from16(uint32_t bits) {
-  if constexpr (BF) return __uint_as_float(bits << 16);
-  else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
 __device__ __forceinline__ uint32_t swz_xor4(uint32_t x) {
@@ -258,10 +264,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
             const float e0 = __builtin_amdgcn_exp2f(p[mb][i] - m[nb]);
             const float e1 = __builtin_amdgcn_exp2f(p[mb][i + 1] - m[nb]);
             l[nb] += e0 + e1;
-            const uint32_t h0 = to16<BF>(e0), h1 = to16<BF>(e1);
-            const uint32_t l0 = to16<BF>(e0 - from16<BF>(h0)), l1 = to16<BF>(e1 - from16<BF>(h1));
-            hw[mb * 2 + i / 2] = h0 | (h1 << 16);
-            lw[mb * 2 + i / 2] = l0 | (l1 << 16);
+            split_pair<BF>(e0, e1, hw[mb * 2 + i / 2], lw[mb * 2 + i / 2]);
           }
         phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);

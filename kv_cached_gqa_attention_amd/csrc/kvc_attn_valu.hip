@@ -10,43 +10,60 @@
 // without grouping, G * T flop per byte with it), so the kernel is built to
 // stream K and V once at full HBM rate:
 //
-//  * A row of K (or V) is H 16-bit values. LPR lanes share one row, each
-//    holding DPL = H / LPR dims as 16-byte loads, so one wave instruction
-//    reads 64 / LPR whole rows (full 128-byte lines).
-//  * Every lane keeps all R query rows of the unit in registers (packed
-//    16-bit pairs), so each K/V row fetched from HBM is used by all G heads
-//    of its group (and all T block tokens) straight from registers.
+//  * Tiles go from HBM straight into LDS (kvc_dma.h): each wave owns two
+//    slots, [K tile + the unit's query rows] and [V tile]. While it computes
+//    on one, the other's next tile is in flight (the next step's K while it
+//    works on V, and so on, across unit boundaries). Nothing in flight
+//    occupies registers; two workgroups share a CU, so two waves share each
+//    SIMD and one's LDS waits hide under the other's arithmetic.
+//  * A row of K (or V) is H 16-bit values. LPR = 8 lanes share one row, each
+//    reading DPL = H / 8 dims from LDS as 16-byte reads; rows of odd index
+//    have their two halves swapped so the eight rows of one read hit
+//    distinct banks.
+//  * Every lane reads all R query rows of the unit, so each K/V row fetched
+//    from HBM is used by all G heads of its group (and all T block tokens).
 //  * q.k uses v_dot2_f32_{bf16,f16}: two 16-bit products accumulated in fp32
 //    per instruction, no conversion; the LPR partial sums are reduced with
 //    DPP row operations.
 //  * Softmax is the online form in fp32, per lane group; the p.v update
 //    widens V to fp32 (exact) and accumulates in fp32.
-//  * Loads are software-pipelined: the next tile's K is requested right
-//    after the current q.k, its V right after the current p.v.
-//  * A workgroup owns a contiguous range of tiles; its four waves take
-//    alternate tiles, so together they stream one contiguous window (worth
-//    about 15% of bandwidth over four far-apart streams). At a unit boundary
-//    the waves park their states in LDS, combine, and publish a partial; the
-//    next unit's first tiles are requested before that, so the stream does
-//    not drain at the boundary. Work is counted in steps of one tile per
-//    wave, so the four waves always have equal work.
+//  * A workgroup owns a contiguous range of steps; its four waves take
+//    alternate tiles, so together they stream one contiguous window. At a
+//    unit boundary the waves combine their states in LDS and publish the
+//    unit's output or a partial, while the next unit's tiles are in flight.
 #include "kvc_device.h"
+#include "kvc_dma.h"
 #include "kvc_internal.h"
 
 namespace kvc {
 
+// LDS bytes of a wave's two slots: [K tile, 1 KB of query rows], [V tile].
+// (With the prefix table of up to ~470 sequences, two workgroups fit a CU.)
+template <int H>
+constexpr int valu_wave_bytes() { return 2 * TILE * H * 2 + 1024; }
+template <int H>
+constexpr int valu_ring_bytes() { return WAVES * valu_wave_bytes<H>(); }
+__host__ __device__ constexpr size_t prefix_bytes(int B) { return ((size_t)(2 * B + 1) * 4 + 15) & ~(size_t)15; }
+
 // MASKED: a window or draft-tree mask is in use (the general per-key test);
 // otherwise the causal test alone, which keeps the loop leaner.
-template <bool BF, int H, int R, int LPR, bool PAGED, int WPE, bool MASKED>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attn_valu_kernel(AttnArgs a) {
+template <bool BF, int H, int R, bool PAGED, bool MASKED>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_valu_kernel(AttnArgs a) {
+  constexpr int LPR = 8;
   constexpr int DPL = H / LPR;         // dims per lane: 8 or 16
   constexpr int NCH = DPL / 8;         // 16-byte chunks per lane per row
-  constexpr int GROUPS = 64 / LPR;     // rows per wave instruction
+  constexpr int GROUPS = 64 / LPR;     // rows per wave read
   constexpr int RPG = TILE / GROUPS;   // tokens per lane group per tile
   constexpr int SLICE = H / NCH;       // elements covered by one chunk across the group
+  constexpr int ROWB = H * 2;
+  constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  constexpr int NI = TILE * CPR / 64;  // copy instructions per tile
+  constexpr int TILEB = TILE * ROWB;
+  constexpr int VSLOT = TILEB + 1024;  // the V slot's offset
   static_assert(DPL == 8 || DPL == 16, "8 or 16 dims per lane");
+  static_assert(R * ROWB <= 1024, "the query rows fit one copy");
 
-  extern __shared__ int32_t s_pre[];   // [2B + 1]
+  extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];  // [2B + 1], then the rings
   __shared__ float s_m[WAVES * R], s_l[WAVES * R];
   __shared__ float s_o[WAVES * R * H];
   __shared__ float s_w[(WAVES + 2) * R];
@@ -62,80 +79,66 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int grp = lane / LPR;
   const int li = lane % LPR;
-  const int lane_off = li * 16;  // byte offset of this lane's first 8 dims in a row
-  const int bmask = (1 << a.block_shift) - 1;
+  char* ring = reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B) + wave * valu_wave_bytes<H>();
+  const uint32_t ring_lds = lds_addr(ring);
 
+  // Swizzle of 16-byte chunk positions: odd rows swap their halves (H = 128).
+  auto swz = [](int r) { return H == 128 ? (r & 1) << 3 : 0; };
+  // This lane's LDS offsets of its chunks c of row grp (add ROWB * GROUPS * i
+  // for row grp + GROUPS * i).
+  int koff[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) koff[c] = grp * ROWB + 16 * ((li + 8 * c) ^ swz(grp));
+
+  // Copy issue: K half of step x = [K tile, query rows], V half = [V tile].
   auto kbase = [&](const Segment& g) {
     return a.k + (int64_t)g.k * a.stride_head + (PAGED ? 0 : (int64_t)g.b * a.stride_seq);
   };
   auto vbase = [&](const Segment& g) {
     return a.v + (int64_t)g.k * a.stride_head + (PAGED ? 0 : (int64_t)g.b * a.stride_seq);
   };
-  // Byte offset of token `tok` of sequence g.b (clamped to its last valid
-  // row, and under a window to its first visible one); an out-of-range block
-  // entry reads block 0 and flags the unit.
-  auto row_off = [&](const Segment& g, int tok, bool& bad) -> int64_t {
-    tok = min(tok, g.seq_len - 1);
-    if constexpr (MASKED) tok = max(tok, first_visible(a, g.seq_len));
-    if constexpr (PAGED) {
-      int blk = a.table[(int64_t)g.b * a.max_blocks + (tok >> a.block_shift)];
-      if ((unsigned)blk >= (unsigned)a.num_blocks) {
-        bad = true;
-        blk = 0;
-      }
-      return (int64_t)blk * a.stride_seq + (int64_t)(tok & bmask) * a.stride_tok + lane_off;
-    } else {
-      return (int64_t)tok * a.stride_tok + lane_off;
-    }
+  uint32_t lvoff[NI];
+  tile_lane_offsets<H>(a, lane, swz, lvoff);
+  // the unit's R query rows, row-major after the K tile: this lane's 16 bytes
+  uint32_t qoff;
+  {
+    const int rq = min(lane * 16 / ROWB, R - 1);
+    const int t = rq / a.G;
+    qoff = (uint32_t)(((int64_t)t * a.N + (rq - t * a.G)) * ROWB + (lane * 16) % ROWB);
+  }
+  // Bad-entry flags of the segment computed and of the next one (the copies
+  // run one step ahead), indexed by segment ordinal parity.
+  bool bad2[2] = {false, false};
+  auto issue_k = [&](const StepCursor& c) {
+    bool bad = false;
+    copy_tile<H, PAGED, MASKED>(a, c.s, kbase(c.s), c.tile(wave), ring_lds, lane, swz, lvoff, bad);
+    dma16(a.q + row_index(a, c.s.b, c.s.k, 0) * ROWB, qoff, ring_lds + TILEB);
+    bad2[c.ord & 1] |= bad;
   };
-  auto load_rows = [&](const char* base, const Segment& g, int tile, uint4 (&dst)[RPG][NCH],
-                       bool& bad) {
-#pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const char* p = base + row_off(g, tile * TILE + grp + GROUPS * i, bad);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) dst[i][c] = load16(p + c * SLICE * 2);
-    }
+  auto issue_v = [&](const StepCursor& c) {
+    bool bad = false;
+    copy_tile<H, PAGED, MASKED>(a, c.s, vbase(c.s), c.tile(wave), ring_lds + VSLOT, lane, swz, lvoff, bad);
+    bad2[c.ord & 1] |= bad;
   };
-  Segment cur = find_segment(a, s_pre, part, part.lo);
-  int64_t x_next = part.lo + (cur.t_end - cur.t_begin);
 
-  // A unit's query rows, this lane's dims. They are loaded again with every
-  // K prefetch (the rows of the unit the prefetched tile belongs to; they
-  // stay in L1), so the query loads are never newer than the tile loads and
-  // waiting for them never waits for a tile prefetch. At a unit switch this
-  // brings in the next unit's rows during the publish of the current one.
-  uint4 qreg[R][NCH];
-  auto load_q = [&](const Segment& g) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const char* qrow = a.q + row_index(a, g.b, g.k, r) * (H * 2);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) qreg[r][c] = load16(qrow + c * SLICE * 2 + li * 16);
-    }
-  };
-  load_q(cur);
-  bool bad_cur = false, bad_nxt = false;
-  uint4 kr[RPG][NCH], vr[RPG][NCH];
-  load_rows(kbase(cur), cur, cur.t_begin * WAVES + wave, kr, bad_cur);
-  __builtin_amdgcn_sched_barrier(0);
-  load_rows(vbase(cur), cur, cur.t_begin * WAVES + wave, vr, bad_cur);
-  __builtin_amdgcn_sched_barrier(0);
+  StepCursor cs, cn;  // the step computed, the next one (whose copies are issued)
+  cs.begin(a, s_pre, part, part.lo);
+  cn = cs;
+  issue_k(cn);
+  issue_v(cn);
+  cn.advance(a, s_pre, part);
 
   SharedUnits shared;
   while (true) {
-    const bool has_next = x_next < part.hi;
-    const Segment nxt = has_next ? find_segment(a, s_pre, part, x_next) : cur;
-    // Row r = t * G + g is new token t. Tiles wholly inside [mask_lo,
-    // mask_hi) are visible to every row; others take the per-key test
-    // (causal or tree rule among the new rows, window at the start).
-    const int new0 = cur.seq_len - a.T;
+    // ---- a new segment: its masks and state
+    const Segment g = cs.s;
+    const int new0 = g.seq_len - a.T;
     const int mask_hi = MASKED && a.tree ? new0 : new0 + 1;
-    const int mask_lo = MASKED && a.window > 0 ? cur.seq_len - a.window : INT_MIN;
+    const int mask_lo = MASKED && a.window > 0 ? g.seq_len - a.window : INT_MIN;
     uint32_t tword[R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      tword[r] = MASKED && a.tree ? a.tree[(int64_t)cur.b * a.T + r / a.G] : 0u;
+      tword[r] = MASKED && a.tree ? load_uniform(a.tree, (int64_t)g.b * a.T + r / a.G) : 0u;
 
     float m[R], l[R], o[R][DPL];
 #pragma unroll
@@ -145,46 +148,50 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
       for (int d = 0; d < DPL; ++d) o[r][d] = 0.f;
     }
-    for (int st = cur.t_begin; st < cur.t_end; ++st) {
-      const int ti = st * WAVES + wave;  // this wave's tile of step st
+    for (;;) {
+      const int64_t x = cs.x;
+      const bool more = x + 1 < part.hi;
+      const char* kslot = ring;
+      const char* vslot = ring + VSLOT;
+      // ---- K half of step x: the one later copy is its V half
+      wait_vm<NI>();
+      uint4 qreg[R][NCH], kr[RPG][NCH];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          qreg[r][c] = *reinterpret_cast<const uint4*>(kslot + TILEB + r * ROWB + (c * SLICE + li * 8) * 2);
+#pragma unroll
+      for (int i = 0; i < RPG; ++i)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          kr[i][c] = *reinterpret_cast<const uint4*>(kslot + koff[c] + i * GROUPS * ROWB);
       // ---- scores (base 2)
       float sc[R][RPG];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        uint4 q4[NCH];
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) q4[c] = qreg[r][c];
+      for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {
           float acc = 0.f;
 #pragma unroll
           for (int c = 0; c < NCH; ++c) {
-            acc = dot2<BF>(kr[i][c].x, q4[c].x, acc);
-            acc = dot2<BF>(kr[i][c].y, q4[c].y, acc);
-            acc = dot2<BF>(kr[i][c].z, q4[c].z, acc);
-            acc = dot2<BF>(kr[i][c].w, q4[c].w, acc);
+            acc = dot2<BF>(kr[i][c].x, qreg[r][c].x, acc);
+            acc = dot2<BF>(kr[i][c].y, qreg[r][c].y, acc);
+            acc = dot2<BF>(kr[i][c].z, qreg[r][c].z, acc);
+            acc = dot2<BF>(kr[i][c].w, qreg[r][c].w, acc);
           }
           sc[r][i] = acc;
         }
-      }
-      // ---- this wave's next tile: in the next step of this unit, else in
-      // the next unit's first step, else this tile again (cached). Loads are
-      // unconditional: a conditional load costs register copies.
-      const bool hop = has_next && st + 1 == cur.t_end;
-      const Segment& ng = hop ? nxt : cur;
-      const int tn = (hop ? nxt.t_begin : min(st + 1, cur.t_end - 1)) * WAVES + wave;
-      const char* nkb = hop ? kbase(nxt) : kbase(cur);
-      const char* nvb = hop ? vbase(nxt) : vbase(cur);
-      bool nbad = false;
-      load_q(ng);
-      load_rows(nkb, ng, tn, kr, nbad);
+      // ---- the K slot is free: the next step's K half goes there
+      wait_lds();
+      if (more) issue_k(cn);
 #pragma unroll
       for (int i = 0; i < RPG; ++i)
 #pragma unroll
         for (int r = 0; r < R; ++r) sc[r][i] = group_sum<LPR>(sc[r][i]) * a.scale_log2;
 
       // ---- mask (only a unit's first and last tiles)
-      const int tok0 = ti * TILE;
+      const int tok0 = cs.tile(wave) * TILE;
       if (tok0 + TILE > mask_hi || tok0 < mask_lo) {
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {
@@ -231,12 +238,14 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
         }
       }
 
-      // ---- p.v
+      // ---- V half of step x: later copies are the next step's K half
+      if (more) wait_vm<NI + 1>(); else wait_vm<0>();
 #pragma unroll
       for (int i = 0; i < RPG; ++i) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          const uint32_t w4[4] = {vr[i][c].x, vr[i][c].y, vr[i][c].z, vr[i][c].w};
+          const uint4 vr = *reinterpret_cast<const uint4*>(vslot + koff[c] + i * GROUPS * ROWB);
+          const uint32_t w4[4] = {vr.x, vr.y, vr.z, vr.w};
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const float v0 = lo_f<BF>(w4[w]);
@@ -249,9 +258,14 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
           }
         }
       }
-      // ---- next tile's V
-      load_rows(nvb, ng, tn, vr, nbad);
-      if (hop) bad_nxt |= nbad; else bad_cur |= nbad;
+      // ---- the V slot is free: the next step's V half goes there
+      wait_lds();
+      if (more) {
+        issue_v(cn);
+        cn.advance(a, s_pre, part);
+      }
+      if (x + 1 == cs.end) break;  // segment done (also at the range's end)
+      cs.advance(a, s_pre, part);
     }
 
     // ---- combine this wave's lane groups, park the wave's state in LDS
@@ -276,22 +290,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
       }
     }
     {
-      const unsigned long long anybad = __builtin_amdgcn_ballot_w64(bad_cur);
+      const bool bad = bad2[cs.ord & 1];
+      bad2[cs.ord & 1] = false;
+      const unsigned long long anybad = __builtin_amdgcn_ballot_w64(bad);
       if (lane == 0) s_bad[wave] = anybad != 0ull;
     }
     __syncthreads();
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    // The next unit's first tiles are in flight while the workgroup combines
-    // and writes this one.
-    finish_segment<H, WAVES>(a, cur, blockIdx.x, s_m, s_l, s_o, s_w, segbad, shared);
+    finish_segment<H, WAVES>(a, g, blockIdx.x, s_m, s_l, s_o, s_w, segbad, shared);
 
-    if (!has_next) break;
-    cur = nxt;
-    x_next += nxt.t_end - nxt.t_begin;
-    bad_cur = bad_nxt;
-    bad_nxt = false;
+    if (cs.x + 1 >= part.hi) break;
+    cs.advance(a, s_pre, part);
   }
   count_and_merge<H>(a, shared, s_flag);
 }
@@ -300,15 +311,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(WPE, WP
 
 template <bool BF, int H, int R, bool PAGED, bool MASKED>
 static hipError_t launch_valu_t(const AttnArgs& a, hipStream_t stream) {
-  constexpr int LPR = 8;
-  // Two waves per SIMD (at most 256 registers per lane) wherever the loop
-  // fits without spilling: every shape except H = 128 with more than four
-  // rows, which goes to the matrix cores anyway.
-  constexpr int WPE = (H == 128 && R <= 4) || H == 64 ? 2 : 1;
-  const size_t shmem = (size_t)(2 * a.B + 1) * sizeof(int32_t);
-  // one worker per workgroup; its waves interleave the tiles
-  hipLaunchKernelGGL((attn_valu_kernel<BF, H, R, LPR, PAGED, WPE, MASKED>), dim3(a.W), dim3(THREADS),
-                     shmem, stream, a);
+  const auto kern = attn_valu_kernel<BF, H, R, PAGED, MASKED>;
+  const size_t shmem = prefix_bytes(a.B) + valu_ring_bytes<H>();
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(prefix_bytes(4096) + valu_ring_bytes<H>()));
+  if (attr != hipSuccess) return attr;
+  // one worker per workgroup, one workgroup per CU; its waves interleave the tiles
+  hipLaunchKernelGGL(kern, dim3(a.W), dim3(THREADS), shmem, stream, a);
   return hipGetLastError();
 }
 
@@ -347,6 +356,16 @@ static hipError_t launch_valu_m(const AttnArgs& a, bool bf16, int H, bool paged,
                  : launch_valu_r<false, 64, false, MASKED>(a, stream);
   return paged ? launch_valu_r<false, 128, true, MASKED>(a, stream)
                : launch_valu_r<false, 128, false, MASKED>(a, stream);
+}
+
+int valu_workgroups_per_cu(int B, int H) {
+  // static LDS (the waves' parked states, R * H <= 512 floats each, and
+  // under 1 KB of row statistics and flags) + prefix table + slots, against
+  // 160 KB
+  constexpr size_t LDS_PER_CU = 160 * 1024;
+  const size_t stat = (size_t)WAVES * 512 * 4 + 1024;
+  const size_t per_wg = stat + prefix_bytes(B) + (H == 64 ? valu_ring_bytes<64>() : valu_ring_bytes<128>());
+  return per_wg * 2 <= LDS_PER_CU ? 2 : 1;
 }
 
 hipError_t launch_attn_valu(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {

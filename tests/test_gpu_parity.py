@@ -271,6 +271,23 @@ def test_one_workspace_serves_calls_of_any_shape(gpu_device):
                     assert np.abs(got - o_ref).max() <= 2e-3, (rep, B, T, N, K, H)
 
 
+@pytest.mark.parametrize("B,T,N,K,H,dtype,layout", [
+    (4096, 1, 4, 2, 64, HF, "contiguous"),  # the largest batch: its prefix table fills LDS
+    (4096, 2, 16, 2, 128, BF, "paged"),     # the same on the matrix cores (G*T = 16)
+    (600, 1, 32, 8, 128, BF, "paged"),      # one vector-ALU workgroup per CU
+])
+def test_large_batches(gpu_device, B, T, N, K, H, dtype, layout):
+    """Batches up to the 4096-sequence limit: the per-workgroup prefix table
+    grows with B and takes LDS from the staging slots' share; sampled units
+    against the oracle."""
+    prior = np.random.default_rng(B + T).integers(0, 300, size=B)
+    run = run_case(B, T, N, K, H, dtype, prior, layout=layout, seed=B + 3 * T)
+    rng = np.random.default_rng(7)
+    units = [(int(b), int(k)) for b, k in zip(rng.integers(0, B, 48), rng.integers(0, K, 48))]
+    units += [(0, 0), (B - 1, K - 1)]
+    compare_units(run, units)
+
+
 # ----------------------------------------------------------------- fused append + attend
 
 FUSED = [SMALL[0], SMALL[3], SMALL[5], SMALL[7], SMALL[9], SMALL[11], SMALL[12], SMALL[13]]
