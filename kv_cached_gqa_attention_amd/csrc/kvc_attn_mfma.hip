@@ -10,13 +10,22 @@
 // Computing the transposed score block puts a query row in a lane column, so
 // its running max needs only two cross-lane steps, and P^T leaves the
 // accumulators already in the B-operand layout of the p.v product (the
-// token-to-k-slot map is chosen to make that true). V^T needs each lane to
-// hold 8 tokens of one h: eight lanes load 8 token rows and swap 16-bit
-// elements with an 8 x 8 register transpose (swizzle + DPP).
+// token-to-k-slot map is chosen to make that true).
+//
+// K and V tiles go from HBM straight into LDS (kvc_dma.h): each wave runs a
+// ring of two or three tile slots (three when the workgroup's LDS allows),
+// K and V tiles alternating, and keeps all but one slot in flight while it
+// computes on the other, across unit boundaries. The slots' 16-byte chunks
+// are XOR-swizzled per row so that the A-operand reads are free of bank
+// conflicts: K rows are read 16 bytes per lane (one row per lane of a
+// 16-lane group), and V^T comes from ds_read_b64_tr_b16, which hands each
+// lane 4 tokens of one h (the transpose the V^T operand needs) from 8-byte
+// pieces of 4 rows.
 // p is split into a 16-bit high part and a 16-bit remainder, each multiplied
 // by V on the matrix cores, so p.v keeps about 16 bits of p (within 2^-16
 // relative, far inside the 2e-3 gate).
 #include "kvc_device.h"
+#include "kvc_dma.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -58,53 +67,35 @@ __device__ __forceinline__ void split_pair(float e0, float e1, uint32_t& hi, uin
   }
 }
 
-__device__ __forceinline__ uint32_t swz_xor4(uint32_t x) {
-  // ds_swizzle bit-mask mode: and 0x1f, or 0, xor 4 (within 32-lane halves)
-  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x101F);
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// ds_read_b64_tr_b16 at p: within each 16-lane group, lane i's element j is
+// 16-bit element (i % 4) of the 8 bytes that lane 4 j + i / 4 of the group
+// addresses (layout checked on the GPU).
+__device__ __forceinline__ uint2 read_tr16(const lds_char* p) {
+  const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)p);
+  return __builtin_bit_cast(uint2, r);
 }
 
-// 8 x 8 transpose of 16-bit elements across the 8 lanes of an aligned lane
-// octet: lane i holds x_i[0..7] (element 2w in the low half of word w), and
-// receives y_i[j] = x_j[i]. Block swaps of 4, 2, then 1 element(s).
-__device__ __forceinline__ uint4 transpose8(uint4 v, int i8) {
-  // Per-lane choices are selects, not branches (every lane runs both sides
-  // of a divergent branch anyway).
-  uint32_t x0 = v.x, x1 = v.y, x2 = v.z, x3 = v.w;
-  const bool b2 = (i8 & 4) != 0, b1 = (i8 & 2) != 0, b0 = (i8 & 1) != 0;
-  uint32_t r0 = swz_xor4(b2 ? x0 : x2), r1 = swz_xor4(b2 ? x1 : x3);
-  x0 = b2 ? r0 : x0;
-  x1 = b2 ? r1 : x1;
-  x2 = b2 ? x2 : r0;
-  x3 = b2 ? x3 : r1;
-  r0 = dpp_u<DPP_QUAD_XOR2>(b1 ? x0 : x1);
-  r1 = dpp_u<DPP_QUAD_XOR2>(b1 ? x2 : x3);
-  x0 = b1 ? r0 : x0;
-  x2 = b1 ? r1 : x2;
-  x1 = b1 ? x1 : r0;
-  x3 = b1 ? x3 : r1;
-  const uint32_t p0 = dpp_u<DPP_QUAD_XOR1>(x0), p1 = dpp_u<DPP_QUAD_XOR1>(x1);
-  const uint32_t p2 = dpp_u<DPP_QUAD_XOR1>(x2), p3 = dpp_u<DPP_QUAD_XOR1>(x3);
-  // v_perm_b32(S0 = own word, S1 = partner's word): bytes 0-3 index S1,
-  // 4-7 index S0. Odd lanes keep their high half and take the partner's
-  // high half as low half ([p2 p3 x2 x3]); even lanes keep their low half
-  // and take the partner's low half as high half ([x0 x1 p0 p1]).
-  const uint32_t sel = b0 ? 0x07060302u : 0x01000504u;
-  x0 = __builtin_amdgcn_perm(x0, p0, sel);
-  x1 = __builtin_amdgcn_perm(x1, p1, sel);
-  x2 = __builtin_amdgcn_perm(x2, p2, sel);
-  x3 = __builtin_amdgcn_perm(x3, p3, sel);
-  return make_uint4(x0, x1, x2, x3);
-}
+// LDS bytes of one staging slot (a K or V tile).
+template <int H>
+constexpr int mfma_tile_bytes() { return TILE * H * 2; }
 
 // MASKED: a window or draft-tree mask is in use (the general per-key test);
-// otherwise the causal test alone.
+// otherwise the causal test alone. nslots: staging slots per wave (2 or 3).
 template <bool BF, int H, int NB, bool PAGED, bool MASKED>
-__global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslots) {
   constexpr int RMAX = NB * 16;  // query rows per unit (row block)
   constexpr int KS = H / 32;     // k-steps of S^T over h
   constexpr int MH = H / 16;     // 16-row h blocks of O^T
+  constexpr int ROWB = H * 2;
+  constexpr int NI = TILE * ROWB / 1024;  // copy instructions per tile
+  constexpr int TILEB = mfma_tile_bytes<H>();
 
-  extern __shared__ int32_t s_pre[];  // [2B + 1]
+  extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];  // [2B + 1], then the slots
   __shared__ float s_m[RMAX], s_l[RMAX];
   __shared__ float s_o[RMAX * H];
   __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[2];
@@ -113,21 +104,101 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
   fill_invalid<H>(a);
   const Partition part = make_partition(a, s_pre, blockIdx.x);
   append_owned<H, THREADS, PAGED>(a, s_pre, part);
+  if (part.lo >= part.hi) return;  // the whole workgroup: no barrier is skipped
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int c = lane & 15;   // column (query row) / A-row (token or h) within a 16 block
   const int g = lane >> 4;   // k-slot group
-  const int i8 = lane & 7;   // lane within its transpose octet
-  const int hb = c >> 3;     // which 8 of the 16 h of a block this octet loads
-  // token of k-slot (g, j): j < 4 -> 4g + j ; j >= 4 -> 16 + 4g + (j - 4)
-  const int vtok = (i8 < 4) ? (4 * g + i8) : (16 + 4 * g + i8 - 4);
+  char* ring = reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B) + wave * nslots * TILEB;
+  const uint32_t ring_lds = lds_addr(ring);
+  const lds_char* ring3 = (const lds_char*)ring;
 
+  // Chunk swizzles (16-byte chunk j of row r sits at position j ^ swz(r)):
+  // K: the 16 rows one A-operand read touches at one column fall in 16
+  // distinct bank groups; V: the 8 rows x 2 chunks of one transposed read of
+  // 32 lanes do.
+  auto swz_k = [](int r) { return H == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto swz_v = [](int r) { return H == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+  uint32_t lvk[NI], lvv[NI];
+  tile_lane_offsets<H>(a, lane, swz_k, lvk);
+  tile_lane_offsets<H>(a, lane, swz_v, lvv);
+  // A operand of S^T: K row 16 mb + c, dims 32 ks + 8 g .. + 7 (chunk 4 ks + g);
+  // swz_k(16 mb + c) == swz_k(c).
+  uint32_t koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = c * ROWB + 16 * ((4 * ks + g) ^ swz_k(c));
+  // A operand of O^T += V^T . P^T, k-slot (g, j) = token 4 g + j (j < 4) or
+  // 16 + 4 g + j - 4: two transposed reads per 16-h block, lane 4 a + b of
+  // group g addressing row 4 g + a (then + 16), dims 16 mh + 4 b .. + 3;
+  // swz_v(r + 16) == swz_v(r).
+  uint32_t voff[MH];
+  {
+    const int r = 4 * g + (c >> 2);
+    const int b = c & 3;
+#pragma unroll
+    for (int mh = 0; mh < MH; ++mh)
+      voff[mh] = r * ROWB + 16 * ((2 * mh + (b >> 1)) ^ swz_v(r)) + 8 * (b & 1);
+  }
+
+  // ---- copies: halves K(x), V(x) of steps x = lo, lo + 1, ... in slot order
+  const int nhalves = (int)(2 * (part.hi - part.lo));
+  int hp = 0;         // halves issued
+  int pslot = 0;      // slot of the next one
+  bool pv = false;    // next one is a V half
+  int bad_bits = 0;   // bad block entries, by segment ordinal mod 4
+  StepCursor pc;
+  pc.begin(a, s_pre, part, part.lo, wave);
+  auto issue_next = [&]() {
+    const uint32_t dst = ring_lds + pslot * TILEB;
+    bool bad = false;
+    if (!pv) {
+      copy_tile<H, PAGED, MASKED>(a, pc.s, pc.kb, pc.tok0, dst, lane, swz_k, lvk, bad);
+    } else {
+      copy_tile<H, PAGED, MASKED>(a, pc.s, pc.vb, pc.tok0, dst, lane, swz_v, lvv, bad);
+    }
+    bad_bits |= (bad ? 1 : 0) << (pc.ord & 3);
+    if (pv) pc.advance(a, s_pre, part);
+    pv = !pv;
+    ++hp;
+    pslot = pslot + 1 == nslots ? 0 : pslot + 1;
+  };
+  for (int i = 0; i < nslots && hp < nhalves; ++i) issue_next();
+  int hc = 0;      // halves consumed
+  int cslot = 0;   // slot of the next one
+  // Wait for half hc + ahead: the halves issued after it are in flight (at
+  // most 2).
+  auto wait_half = [&](int ahead) {
+    const int later = hp - 1 - hc - ahead;
+    if (later >= 2) wait_vm<2 * NI>(); else if (later == 1) wait_vm<NI>(); else wait_vm<0>();
+  };
+  auto release_half = [&]() {
+    wait_lds();  // its reads have returned: the slot can be refilled
+    if (hp < nhalves) issue_next();
+    ++hc;
+    cslot = cslot + 1 == nslots ? 0 : cslot + 1;
+  };
+
+  // A operand of S^T for the next tile, read from LDS a tile ahead (while
+  // the previous tile's p.v products run)
+  uint4 kf[2][KS];
+  auto read_k = [&](int ahead) {  // K tile of half hc + ahead
+    wait_half(ahead);
+    const int slot = cslot + ahead >= nslots ? cslot + ahead - nslots : cslot + ahead;
+    const char* kt = ring + slot * TILEB;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[mb][ks] = *reinterpret_cast<const uint4*>(kt + koff[ks] + mb * 16 * ROWB);
+  };
+  read_k(0);
+
+  StepCursor cs;
+  cs.begin(a, s_pre, part, part.lo, wave);
   SharedUnits shared;
-  for (int64_t x = part.lo; x < part.hi;) {
-    const Segment s = find_segment(a, s_pre, part, x);
-    x += s.t_end - s.t_begin;
-
+  while (true) {
+    const Segment s = cs.s;
     // Q^T fragments (B operand): query row rb*RMAX + 16 nb + c, h = 32 ks + 8 g + j.
     uint4 qf[NB][KS];
     int tq[NB];         // new-token index of this lane's query column
@@ -147,29 +218,10 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
       }
       tw[nb] = MASKED && a.tree ? a.tree[(int64_t)s.b * a.T + tq[nb]] : 0u;
     }
+    // Every outstanding load (these and the copies in flight) has landed,
+    // so no wait for the query loads falls inside the tile loop.
+    wait_stores();
 
-    const char* kb = a.k + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
-    const char* vb = a.v + (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
-    const int32_t* trow = PAGED ? a.table + (int64_t)s.b * a.max_blocks : nullptr;
-    const int bmask = (1 << a.block_shift) - 1;
-    bool bad = false;
-    const int vis0 = MASKED ? first_visible(a, s.seq_len) : 0;
-    auto row_off = [&](int tok) -> int64_t {
-      tok = min(tok, s.seq_len - 1);
-      if constexpr (MASKED) tok = max(tok, vis0);
-      if constexpr (PAGED) {
-        int blk = trow[tok >> a.block_shift];
-        if ((unsigned)blk >= (unsigned)a.num_blocks) {
-          bad = true;
-          blk = 0;
-        }
-        return (int64_t)blk * a.stride_seq + (int64_t)(tok & bmask) * a.stride_tok;
-      } else {
-        return (int64_t)tok * a.stride_tok;
-      }
-    };
-
-    uint4 kf[2][KS], vf[MH];
     floatx4 ot[MH][NB];
 #pragma unroll
     for (int mh = 0; mh < MH; ++mh)
@@ -181,29 +233,9 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
       m[nb] = NEG_BIG;
       l[nb] = 0.f;
     }
+    const int new0 = s.seq_len - a.T;
 
-    auto load_k = [&](int tile) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int64_t off = row_off(tile * TILE + mb * 16 + c);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[mb][ks] = load16(kb + off + (ks * 32 + g * 8) * 2);
-      }
-    };
-    auto load_v = [&](int tile) {
-      const int64_t offv = row_off(tile * TILE + vtok);
-#pragma unroll
-      for (int mh = 0; mh < MH; ++mh) vf[mh] = load16(vb + offv + (mh * 16 + hb * 8) * 2);
-    };
-    // Work comes in steps of one tile per wave, so the four waves have equal
-    // work; tiles past the unit's end are masked (their loads are clamped).
-    load_k(s.t_begin * WAVES + wave);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(s.t_begin * WAVES + wave);
-    __builtin_amdgcn_sched_barrier(0);
-
-    for (int sp = s.t_begin; sp < s.t_end; ++sp) {
-      const int ti = sp * WAVES + wave;
+    for (;;) {
       // ---- S^T = K . Q^T
       floatx4 st[2][NB];
 #pragma unroll
@@ -215,22 +247,19 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
           for (int ks = 0; ks < KS; ++ks) acc = mfma16<BF>(kf[mb][ks], qf[nb][ks], acc);
           st[mb][nb] = acc;
         }
-
-      // ---- next tile's K (past the segment: this tile again, cached)
-      const int tn = min(sp + 1, s.t_end - 1) * WAVES + wave;
-      load_k(tn);
+      release_half();
 
       // ---- scale, mask, online softmax (one query row per lane column)
-      const int tok0 = ti * TILE;
-      const int new0 = s.seq_len - a.T;
+      const int tok0 = cs.tok0;
       // tiles wholly inside [new0 + 1 (new0 with a tree), seq_len - window)
       // are visible to every query
       const bool edge = tok0 + TILE > (MASKED && a.tree ? new0 : new0 + 1) ||
                         (MASKED && a.window > 0 && tok0 < s.seq_len - a.window);
-      uint4 phi[NB], plo[NB];
+      // All column blocks at once (independent chains side by side), one
+      // wave-uniform decision whether any running max moves.
+      float p[NB][2][4], mt[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        float p[2][4];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -239,59 +268,79 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
             const int tok = tok0 + mb * 16 + 4 * g + i;
             if (edge && !(MASKED ? key_visible(a, tok, new0, tq[nb], tw[nb]) : tok <= new0 + tq[nb]))
               v = -__builtin_inff();
-            p[mb][i] = v;
+            p[nb][mb][i] = v;
           }
-        float mt = p[0][0];
+        mt[nb] = fmaxf(fmaxf(fmaxf(p[nb][0][0], p[nb][0][1]), fmaxf(p[nb][0][2], p[nb][0][3])),
+                       fmaxf(fmaxf(p[nb][1][0], p[nb][1][1]), fmaxf(p[nb][1][2], p[nb][1][3])));
+      }
+      bool grow = false;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int nb = 0; nb < NB; ++nb) {
+        mt[nb] = max_cols4(mt[nb]);
+        grow |= mt[nb] > m[nb] + RESCALE_MARGIN;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, p[mb][i]);
-        mt = fmaxf(mt, shfl_xor_f(mt, 16));
-        mt = fmaxf(mt, shfl_xor_f(mt, 32));
-        if (__builtin_amdgcn_ballot_w64(mt > m[nb] + RESCALE_MARGIN) != 0ull) {
-          const float mn = mt > m[nb] + RESCALE_MARGIN ? mt : m[nb];
-          const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);
+        for (int nb = 0; nb < NB; ++nb) {
+          const float mn = mt[nb] > m[nb] + RESCALE_MARGIN ? mt[nb] : m[nb];
+          const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);  // 1 where unchanged
           l[nb] *= alpha;
 #pragma unroll
           for (int mh = 0; mh < MH; ++mh) ot[mh][nb] *= alpha;
           m[nb] = mn;
         }
+      }
+      uint4 phi[NB], plo[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; i += 2) {
-            const float e0 = __builtin_amdgcn_exp2f(p[mb][i] - m[nb]);
-            const float e1 = __builtin_amdgcn_exp2f(p[mb][i + 1] - m[nb]);
+            const float e0 = __builtin_amdgcn_exp2f(p[nb][mb][i] - m[nb]);
+            const float e1 = __builtin_amdgcn_exp2f(p[nb][mb][i + 1] - m[nb]);
             l[nb] += e0 + e1;
             split_pair<BF>(e0, e1, hw[mb * 2 + i / 2], lw[mb * 2 + i / 2]);
           }
         phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
+      // ---- V^T of this tile, and the next tile's K (possibly of the next
+      // unit), read before the p.v products
+      wait_half(0);
+      const lds_char* vt_base = ring3 + cslot * TILEB;
+      uint4 vt[MH];
+#pragma unroll
+      for (int mh = 0; mh < MH; ++mh) {
+        const uint2 lo4 = read_tr16(vt_base + voff[mh]);
+        const uint2 hi4 = read_tr16(vt_base + voff[mh] + 16 * ROWB);
+        vt[mh] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+      }
+      if (cs.x + 1 < part.hi) read_k(1);
 
       // ---- O^T += V^T . P^T
 #pragma unroll
       for (int mh = 0; mh < MH; ++mh) {
-        const uint4 vt = transpose8(vf[mh], i8);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          ot[mh][nb] = mfma16<BF>(vt, phi[nb], ot[mh][nb]);
-          ot[mh][nb] = mfma16<BF>(vt, plo[nb], ot[mh][nb]);
+          ot[mh][nb] = mfma16<BF>(vt[mh], phi[nb], ot[mh][nb]);
+          ot[mh][nb] = mfma16<BF>(vt[mh], plo[nb], ot[mh][nb]);
         }
       }
-
-      // ---- next tile's V
-      load_v(tn);
+      release_half();  // the V slot: the products have their operands
+      if (cs.x + 1 == cs.end) break;  // segment done (also at the range's end)
+      cs.advance(a, s_pre, part);
     }
 
     // ---- per-column totals of l (lanes of one column hold different tokens)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      l[nb] += shfl_xor_f(l[nb], 16);
-      l[nb] += shfl_xor_f(l[nb], 32);
+      l[nb] = sum_cols4(l[nb]);
     }
     {
+      const bool bad = (bad_bits >> (cs.ord & 3)) & 1;
+      bad_bits &= ~(1 << (cs.ord & 3));
       const unsigned long long anybad = __ballot(bad);
       if (lane == 0) s_bad[wave] = anybad != 0ull;
     }
@@ -327,6 +376,8 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
     finish_segment<H, 1>(a, s, blockIdx.x, s_m, s_l, s_o, s_m, segbad, shared);
+    if (cs.x + 1 >= part.hi) break;
+    cs.advance(a, s_pre, part);
   }
   count_and_merge<H>(a, shared, s_flag);
 }
@@ -335,10 +386,26 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a) {
 
 template <bool BF, int H, int NB, bool PAGED, bool MASKED>
 static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
-  const size_t shmem = (size_t)(2 * a.B + 1) * sizeof(int32_t);
+  constexpr int LDS_PER_CU = 160 * 1024;
+  const auto kern = attn_mfma_kernel<BF, H, NB, PAGED, MASKED>;
+  static size_t static_lds = 0;
+  static const hipError_t attr = [&] {
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, (const void*)kern);
+    if (e != hipSuccess) return e;
+    static_lds = fa.sharedSizeBytes;
+    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)(LDS_PER_CU - static_lds));
+  }();
+  if (attr != hipSuccess) return attr;
+  // three slots per wave where the LDS allows (the prefix table grows with B)
+  const size_t pre = prefix_bytes(a.B);
+  const size_t slots3 = (size_t)WAVES * 3 * mfma_tile_bytes<H>();
+  const int nslots = static_lds + pre + slots3 <= (size_t)LDS_PER_CU ? 3 : 2;
+  const size_t shmem = pre + (size_t)WAVES * nslots * mfma_tile_bytes<H>();
+  if (static_lds + shmem > (size_t)LDS_PER_CU) return hipErrorInvalidConfiguration;
   // one worker per workgroup
-  hipLaunchKernelGGL((attn_mfma_kernel<BF, H, NB, PAGED, MASKED>), dim3(a.W), dim3(THREADS), shmem,
-                     stream, a);
+  hipLaunchKernelGGL(kern, dim3(a.W), dim3(THREADS), shmem, stream, a, nslots);
   return hipGetLastError();
 }
 

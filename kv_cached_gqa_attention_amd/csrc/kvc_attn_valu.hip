@@ -43,7 +43,6 @@ template <int H>
 constexpr int valu_wave_bytes() { return 2 * TILE * H * 2 + 1024; }
 template <int H>
 constexpr int valu_ring_bytes() { return WAVES * valu_wave_bytes<H>(); }
-__host__ __device__ constexpr size_t prefix_bytes(int B) { return ((size_t)(2 * B + 1) * 4 + 15) & ~(size_t)15; }
 
 // MASKED: a window or draft-tree mask is in use (the general per-key test);
 // otherwise the causal test alone, which keeps the loop leaner.
@@ -91,12 +90,6 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int c = 0; c < NCH; ++c) koff[c] = grp * ROWB + 16 * ((li + 8 * c) ^ swz(grp));
 
   // Copy issue: K half of step x = [K tile, query rows], V half = [V tile].
-  auto kbase = [&](const Segment& g) {
-    return a.k + (int64_t)g.k * a.stride_head + (PAGED ? 0 : (int64_t)g.b * a.stride_seq);
-  };
-  auto vbase = [&](const Segment& g) {
-    return a.v + (int64_t)g.k * a.stride_head + (PAGED ? 0 : (int64_t)g.b * a.stride_seq);
-  };
   uint32_t lvoff[NI];
   tile_lane_offsets<H>(a, lane, swz, lvoff);
   // the unit's R query rows, row-major after the K tile: this lane's 16 bytes
@@ -111,18 +104,18 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   bool bad2[2] = {false, false};
   auto issue_k = [&](const StepCursor& c) {
     bool bad = false;
-    copy_tile<H, PAGED, MASKED>(a, c.s, kbase(c.s), c.tile(wave), ring_lds, lane, swz, lvoff, bad);
+    copy_tile<H, PAGED, MASKED>(a, c.s, c.kb, c.tok0, ring_lds, lane, swz, lvoff, bad);
     dma16(a.q + row_index(a, c.s.b, c.s.k, 0) * ROWB, qoff, ring_lds + TILEB);
     bad2[c.ord & 1] |= bad;
   };
   auto issue_v = [&](const StepCursor& c) {
     bool bad = false;
-    copy_tile<H, PAGED, MASKED>(a, c.s, vbase(c.s), c.tile(wave), ring_lds + VSLOT, lane, swz, lvoff, bad);
+    copy_tile<H, PAGED, MASKED>(a, c.s, c.vb, c.tok0, ring_lds + VSLOT, lane, swz, lvoff, bad);
     bad2[c.ord & 1] |= bad;
   };
 
   StepCursor cs, cn;  // the step computed, the next one (whose copies are issued)
-  cs.begin(a, s_pre, part, part.lo);
+  cs.begin(a, s_pre, part, part.lo, wave);
   cn = cs;
   issue_k(cn);
   issue_v(cn);
@@ -191,7 +184,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int r = 0; r < R; ++r) sc[r][i] = group_sum<LPR>(sc[r][i]) * a.scale_log2;
 
       // ---- mask (only a unit's first and last tiles)
-      const int tok0 = cs.tile(wave) * TILE;
+      const int tok0 = cs.tok0;
       if (tok0 + TILE > mask_hi || tok0 < mask_lo) {
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {

@@ -212,6 +212,23 @@ __device__ __forceinline__ float max_groups8(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column of the
+// 16 x 16 matrix-core layouts), on the vector ALU: v_permlane16_swap and
+// v_permlane32_swap with both operands x return the pair {x[l], x[l ^ 16]}
+// (resp. ^ 32) in every lane. Every lane gets the same result.
+__device__ __forceinline__ float max_cols4(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum_cols4(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 // ---------------------------------------------------------------- partition
 
 __device__ __forceinline__ bool seq_valid(int32_t len, int32_t T, int32_t capacity) {

@@ -20,6 +20,13 @@
 
 namespace kvc {
 
+// Bytes of the per-workgroup prefix table (2B + 1 ints, see
+// build_tile_prefix) at the start of dynamic LDS, rounded up so the staging
+// slots after it stay 16-byte aligned.
+__host__ __device__ constexpr size_t prefix_bytes(int B) {
+  return ((size_t)(2 * B + 1) * 4 + 15) & ~(size_t)15;
+}
+
 // LDS byte address of shared storage (the low half of its generic address).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)p;
@@ -29,13 +36,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // unsigned) to LDS lds + 16 * lane. The copy takes its LDS address from m0,
 // which no other instruction of these kernels uses (the compiler is told it
 // is clobbered; the kernels' assembly is checked to hold no other m0 use).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = uniform_u32((uint32_t)u), hi = uniform_u32((uint32_t)(u >> 32));
+  return reinterpret_cast<const char*>(lo | (hi << 32));
+}
+
+// m0 is named as clobbered; clang warns that it is a reserved register.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// (The scalar operands are wave-uniform by construction; readfirstlane
+// states it to the compiler, which otherwise may hold them in vector
+// registers.)
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(lds), "v"(voff), "s"(sbase)
+      : "s"(uniform_u32(lds)), "v"(voff), "s"(uniform_ptr(sbase))
       : "memory", "m0");
 }
 
@@ -46,9 +69,11 @@ __device__ __forceinline__ void dma16_addr(const char* addr, uint32_t lds) {
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off"
       :
-      : "s"(lds), "v"(addr)
+      : "s"(uniform_u32(lds)), "v"(addr)
       : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // Wait until at most N vector memory operations of this wave are outstanding.
 template <int N>
@@ -73,38 +98,48 @@ __device__ __forceinline__ uint32_t load_uniform(const uint32_t* p, int64_t i) {
 }
 
 // A wave's walk over the steps of its workgroup's range, one tile per step,
-// for issuing copies ahead of the compute: the current segment and the tile
-// of the current step.
+// for issuing copies ahead of the compute: the current segment, the first
+// token of this wave's tile at the current step, and the unit's K and V
+// bases (the sequence's rows, or the pool with a block table).
 struct StepCursor {
   int64_t x;      // flat step
-  int64_t start;  // first flat step of the segment
-  int64_t end;    // one past its last
+  int64_t end;    // one past the segment's last
   int ord;        // segments entered before this one
+  int tok0;       // first token of this wave's tile
+  int wave;
+  const char* kb;
+  const char* vb;
   Segment s;
 
-  __device__ void begin(const AttnArgs& a, const int32_t* s_pre, const Partition& p, int64_t x0) {
+  __device__ void begin(const AttnArgs& a, const int32_t* s_pre, const Partition& p, int64_t x0,
+                        int w) {
     x = x0;
     ord = 0;
+    wave = w;
     enter(a, s_pre, p);
   }
   __device__ void advance(const AttnArgs& a, const int32_t* s_pre, const Partition& p) {
     ++x;
+    tok0 += STEP;
     if (x == end && x < p.hi) {
       ++ord;
       enter(a, s_pre, p);
     }
   }
-  __device__ int tile(int wave) const { return (s.t_begin + (int)(x - start)) * WAVES + wave; }
 
  private:
   __device__ void enter(const AttnArgs& a, const int32_t* s_pre, const Partition& p) {
-    start = x;
     s = find_segment(a, s_pre, p, x);
     end = x + (s.t_end - s.t_begin);
+    tok0 = (s.t_begin * WAVES + wave) * TILE;
+    const int64_t off = (int64_t)s.k * a.stride_head + (a.table ? 0 : (int64_t)s.b * a.stride_seq);
+    kb = a.k + off;
+    vb = a.v + off;
   }
 };
 
-// Copy tile `tile` (TILE token rows) of one unit's K or V to LDS at `lds`:
+// Copy the tile of TILE token rows starting at token `first` of one unit's K
+// or V (base: the unit's rows, or the pool) to LDS at `lds`:
 // row r (ROWB = 2H bytes) at lds + r * ROWB, its 16-byte chunk j at position
 // j ^ swz(r) (swz: the kernel's bank-conflict swizzle, an involution on
 // chunk positions). One instruction covers RPI = 64 / (ROWB / 16)
@@ -137,13 +172,12 @@ __device__ __forceinline__ void tile_lane_offsets(const AttnArgs& a, int lane, S
 
 template <int H, bool PAGED, bool MASKED, typename Swz>
 __device__ __forceinline__ void copy_tile(const AttnArgs& a, const Segment& g, const char* base,
-                                          int tile, uint32_t lds, int lane, Swz swz,
+                                          int first, uint32_t lds, int lane, Swz swz,
                                           const uint32_t (&lvoff)[TILE * H * 2 / 1024], bool& bad) {
   constexpr int ROWB = H * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int RPI = 64 / CPR;
   constexpr int NI = TILE / RPI;
-  const int first = tile * TILE;
   const int last = g.seq_len - 1;
   const int vis0 = MASKED ? first_visible(a, g.seq_len) : 0;
   const int64_t trow = PAGED ? (int64_t)g.b * a.max_blocks : 0;
