@@ -30,10 +30,9 @@ constexpr int MFMA_MAX_NB = 4;         // 16-row blocks per matrix-core unit
 // MIN_STEPS_PER_WORKER steps.
 constexpr int SHORT_UNIT_STEPS = 4;
 constexpr int MIN_STEPS_PER_WORKER = 2;
-// Resident workgroups per CU at the kernels' register and LDS use
-// (vector-ALU kernel: 2 waves per SIMD while two workgroups' LDS fits;
-// matrix-core kernel: 1), so an automatic grid is one round of workgroups.
-constexpr int MFMA_WG_PER_CU = 1;
+// An automatic grid is one round of workgroups: as many per CU as the
+// kernel's register and LDS use lets reside (valu_workgroups_per_cu,
+// mfma_workgroups_per_cu).
 constexpr int DEFAULT_CUS = 256;
 // The workspace starts with a fixed-size array of per-unit counters. Only the
 // counter atomics (and their reset to zero by the merging workgroup) ever
@@ -93,7 +92,7 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
     p->W = num_wg > (1 << 20) ? (1 << 20) : num_wg;
   } else {
     const int64_t steps_ub = units * ((max_seq_len + kvc::STEP - 1) / kvc::STEP);
-    const int64_t full = (int64_t)device_cu_count() * (p->mfma ? MFMA_WG_PER_CU : kvc::valu_workgroups_per_cu(B, H));
+    const int64_t full = (int64_t)device_cu_count() * (p->mfma ? kvc::mfma_workgroups_per_cu(B, H, p->RMAX) : kvc::valu_workgroups_per_cu(B, H));
     const int64_t unit_steps = (max_seq_len + kvc::STEP - 1) / kvc::STEP;
     int64_t want_workers = unit_steps <= SHORT_UNIT_STEPS
                                ? units

@@ -84,10 +84,22 @@ __device__ __forceinline__ uint2 read_tr16(const lds_char* p) {
 template <int H>
 constexpr int mfma_tile_bytes() { return TILE * H * 2; }
 
+// Whether two workgroups of the QLDS form fit one CU's LDS: per workgroup
+// the prefix table, the unit's query rows and two slots per wave, the wave
+// fold living in the slots (under 1 KB of other LDS).
+__host__ __device__ constexpr bool mfma_two_per_cu(int B, int H, int RMAX) {
+  return RMAX <= 48 && prefix_bytes(B) + (size_t)RMAX * H * 2 + (size_t)WAVES * 2 * TILE * H * 2 + 1024 <= 80 * 1024;
+}
+
 // MASKED: a window or draft-tree mask is in use (the general per-key test);
 // otherwise the causal test alone. nslots: staging slots per wave (2 or 3).
-template <bool BF, int H, int NB, bool PAGED, bool MASKED>
-__global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslots) {
+// QLDS: two workgroups per CU (two waves per SIMD, so one wave's waits hide
+// under the other's work). To fit, the query rows live in LDS rather than
+// in registers, the copies stop at each unit boundary, and the waves' fold
+// at a unit's end reuses the slots.
+template <bool BF, int H, int NB, bool PAGED, bool MASKED, bool QLDS>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(QLDS ? 2 : 1, QLDS ? 2 : 1)))
+void attn_mfma_kernel(AttnArgs a, int nslots) {
   constexpr int RMAX = NB * 16;  // query rows per unit (row block)
   constexpr int KS = H / 32;     // k-steps of S^T over h
   constexpr int MH = H / 16;     // 16-row h blocks of O^T
@@ -95,9 +107,10 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
   constexpr int NI = TILE * ROWB / 1024;  // copy instructions per tile
   constexpr int TILEB = mfma_tile_bytes<H>();
 
-  extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];  // [2B + 1], then the slots
+  // [2B + 1], (QLDS: the unit's query rows,) then the slots
+  extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];
   __shared__ float s_m[RMAX], s_l[RMAX];
-  __shared__ float s_o[RMAX * H];
+  __shared__ float s_o_own[QLDS ? 4 : RMAX * H];
   __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[2];
 
   build_tile_prefix(a, s_pre, s_wave);
@@ -110,7 +123,10 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int c = lane & 15;   // column (query row) / A-row (token or h) within a 16 block
   const int g = lane >> 4;   // k-slot group
-  char* ring = reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B) + wave * nslots * TILEB;
+  char* qarea = reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B);  // QLDS: RMAX rows, swizzled as K
+  char* ring_all = qarea + (QLDS ? RMAX * ROWB : 0);
+  char* ring = ring_all + wave * nslots * TILEB;
+  float* s_o = QLDS ? reinterpret_cast<float*>(ring_all) : s_o_own;  // the waves' fold
   const uint32_t ring_lds = lds_addr(ring);
   const lds_char* ring3 = (const lds_char*)ring;
 
@@ -142,14 +158,15 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
   }
 
   // ---- copies: halves K(x), V(x) of steps x = lo, lo + 1, ... in slot order
-  const int nhalves = (int)(2 * (part.hi - part.lo));
+  // (QLDS: restarted at every unit boundary)
+  int nhalves = (int)(2 * (part.hi - part.lo));
   int hp = 0;         // halves issued
   int pslot = 0;      // slot of the next one
   bool pv = false;    // next one is a V half
   int bad_bits = 0;   // bad block entries, by segment ordinal mod 4
   StepCursor pc;
   pc.begin(a, s_pre, part, part.lo, wave);
-  auto issue_next = [&]() {
+  auto issue_next = [&]() __attribute__((always_inline)) {
     const uint32_t dst = ring_lds + pslot * TILEB;
     bool bad = false;
     if (!pv) {
@@ -163,16 +180,19 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
     ++hp;
     pslot = pslot + 1 == nslots ? 0 : pslot + 1;
   };
-  for (int i = 0; i < nslots && hp < nhalves; ++i) issue_next();
+  auto prologue = [&]() __attribute__((always_inline)) {
+    for (int i = 0; i < nslots && hp < nhalves; ++i) issue_next();
+  };
+  if (!QLDS) prologue();
   int hc = 0;      // halves consumed
   int cslot = 0;   // slot of the next one
   // Wait for half hc + ahead: the halves issued after it are in flight (at
   // most 2).
-  auto wait_half = [&](int ahead) {
+  auto wait_half = [&](int ahead) __attribute__((always_inline)) {
     const int later = hp - 1 - hc - ahead;
     if (later >= 2) wait_vm<2 * NI>(); else if (later == 1) wait_vm<NI>(); else wait_vm<0>();
   };
-  auto release_half = [&]() {
+  auto release_half = [&]() __attribute__((always_inline)) {
     wait_lds();  // its reads have returned: the slot can be refilled
     if (hp < nhalves) issue_next();
     ++hc;
@@ -182,7 +202,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
   // A operand of S^T for the next tile, read from LDS a tile ahead (while
   // the previous tile's p.v products run)
   uint4 kf[2][KS];
-  auto read_k = [&](int ahead) {  // K tile of half hc + ahead
+  auto read_k = [&](int ahead) __attribute__((always_inline)) {  // K tile of half hc + ahead
     wait_half(ahead);
     const int slot = cslot + ahead >= nslots ? cslot + ahead - nslots : cslot + ahead;
     const char* kt = ring + slot * TILEB;
@@ -192,7 +212,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
       for (int ks = 0; ks < KS; ++ks)
         kf[mb][ks] = *reinterpret_cast<const uint4*>(kt + koff[ks] + mb * 16 * ROWB);
   };
-  read_k(0);
+  if (!QLDS) read_k(0);
 
   StepCursor cs;
   cs.begin(a, s_pre, part, part.lo, wave);
@@ -200,20 +220,24 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
   while (true) {
     const Segment s = cs.s;
     // Q^T fragments (B operand): query row rb*RMAX + 16 nb + c, h = 32 ks + 8 g + j.
-    uint4 qf[NB][KS];
+    uint4 qf[QLDS ? 1 : NB][KS];
     int tq[NB];         // new-token index of this lane's query column
     uint32_t tw[NB];    // its tree word
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int rr = s.rb * RMAX + nb * 16 + c;
       if (rr < a.R) {
-        const char* qrow = a.q + row_index(a, s.b, s.k, rr) * (H * 2);
+        if constexpr (!QLDS) {
+          const char* qrow = a.q + row_index(a, s.b, s.k, rr) * (H * 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = load16(qrow + (ks * 32 + g * 8) * 2);
+          for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = load16(qrow + (ks * 32 + g * 8) * 2);
+        }
         tq[nb] = rr / a.G;
       } else {
+        if constexpr (!QLDS) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = make_uint4(0, 0, 0, 0);
+          for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = make_uint4(0, 0, 0, 0);
+        }
         tq[nb] = a.T - 1;  // padding column: any valid row, discarded
       }
       tw[nb] = MASKED && a.tree ? a.tree[(int64_t)s.b * a.T + tq[nb]] : 0u;
@@ -221,6 +245,29 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
     // Every outstanding load (these and the copies in flight) has landed,
     // so no wait for the query loads falls inside the tile loop.
     wait_stores();
+    if constexpr (QLDS) {
+      // this unit's copies, and its query rows: RMAX rows of ROWB bytes,
+      // chunk j of row r at position j ^ swz_k(r) (rows past R repeat row
+      // R - 1; their columns are discarded); each wave copies a quarter
+      hp = hc = pslot = cslot = 0;
+      pv = false;
+      pc = cs;
+      nhalves = (int)(2 * (cs.end - cs.x));
+      prologue();
+      constexpr int QI = RMAX * ROWB / 1024 / WAVES;  // copy instructions per wave
+      static_assert(RMAX * ROWB % (1024 * WAVES) == 0, "query rows split evenly");
+#pragma unroll
+      for (int i = 0; i < QI; ++i) {
+        const int q = (wave * QI + i) * 64 + lane;  // 16-byte chunk of the area
+        const int r = q / (ROWB / 16);
+        const int j = (q % (ROWB / 16)) ^ swz_k(r);
+        const int rr = min(s.rb * RMAX + r, a.R - 1);
+        dma16_addr(a.q + row_index(a, s.b, s.k, rr) * ROWB + j * 16,
+                   lds_addr(qarea) + (wave * QI + i) * 1024);
+      }
+      wait_vm<0>();
+      __syncthreads();
+    }
 
     floatx4 ot[MH][NB];
 #pragma unroll
@@ -236,7 +283,8 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
     const int new0 = s.seq_len - a.T;
 
     for (;;) {
-      // ---- S^T = K . Q^T
+      // ---- S^T = K . Q^T (one wave per SIMD: K was read a tile ahead)
+      if constexpr (QLDS) read_k(0);
       floatx4 st[2][NB];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -244,7 +292,14 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
         for (int nb = 0; nb < NB; ++nb) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mfma16<BF>(kf[mb][ks], qf[nb][ks], acc);
+          for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (QLDS) {
+              const uint4 qv = *reinterpret_cast<const uint4*>(qarea + nb * 16 * ROWB + koff[ks]);
+              acc = mfma16<BF>(kf[mb][ks], qv, acc);
+            } else {
+              acc = mfma16<BF>(kf[mb][ks], qf[nb][ks], acc);
+            }
+          }
           st[mb][nb] = acc;
         }
       release_half();
@@ -306,26 +361,30 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
         phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
-      // ---- V^T of this tile, and the next tile's K (possibly of the next
-      // unit), read before the p.v products
+      // ---- V^T of this tile, and (one wave per SIMD) the next tile's K,
+      // possibly of the next unit, read before the p.v products
       wait_half(0);
       const lds_char* vt_base = ring3 + cslot * TILEB;
-      uint4 vt[MH];
-#pragma unroll
-      for (int mh = 0; mh < MH; ++mh) {
+      auto read_v = [&](int mh) __attribute__((always_inline)) {
         const uint2 lo4 = read_tr16(vt_base + voff[mh]);
         const uint2 hi4 = read_tr16(vt_base + voff[mh] + 16 * ROWB);
-        vt[mh] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+        return make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+      };
+      uint4 vt[QLDS ? 1 : MH];
+      if constexpr (!QLDS) {
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh) vt[mh] = read_v(mh);
+        if (cs.x + 1 < part.hi) read_k(1);
       }
-      if (cs.x + 1 < part.hi) read_k(1);
 
       // ---- O^T += V^T . P^T
 #pragma unroll
       for (int mh = 0; mh < MH; ++mh) {
+        const uint4 v = QLDS ? read_v(mh) : vt[QLDS ? 0 : mh];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          ot[mh][nb] = mfma16<BF>(vt[mh], phi[nb], ot[mh][nb]);
-          ot[mh][nb] = mfma16<BF>(vt[mh], plo[nb], ot[mh][nb]);
+          ot[mh][nb] = mfma16<BF>(v, phi[nb], ot[mh][nb]);
+          ot[mh][nb] = mfma16<BF>(v, plo[nb], ot[mh][nb]);
         }
       }
       release_half();  // the V slot: the products have their operands
@@ -345,6 +404,7 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
       if (lane == 0) s_bad[wave] = anybad != 0ull;
     }
     // ---- fold the four waves into one state in LDS, one wave at a time
+    if constexpr (QLDS) __syncthreads();  // every wave is done with its slots
     for (int w = 0; w < WAVES; ++w) {
       if (wave == w) {
 #pragma unroll
@@ -379,15 +439,18 @@ __global__ __launch_bounds__(THREADS) void attn_mfma_kernel(AttnArgs a, int nslo
     if (cs.x + 1 >= part.hi) break;
     cs.advance(a, s_pre, part);
   }
-  count_and_merge<H>(a, shared, s_flag);
+  // every copy has landed and every slot has been read: the slots are free
+  __syncthreads();
+  count_and_merge<H>(a, shared, s_flag, reinterpret_cast<float*>(ring_all),
+                     WAVES * nslots * TILEB / 4);
 }
 
 // ---------------------------------------------------------------- launch
 
-template <bool BF, int H, int NB, bool PAGED, bool MASKED>
-static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
+template <bool BF, int H, int NB, bool PAGED, bool MASKED, bool QLDS>
+static hipError_t launch_mfma_q(const AttnArgs& a, hipStream_t stream) {
   constexpr int LDS_PER_CU = 160 * 1024;
-  const auto kern = attn_mfma_kernel<BF, H, NB, PAGED, MASKED>;
+  const auto kern = attn_mfma_kernel<BF, H, NB, PAGED, MASKED, QLDS>;
   static size_t static_lds = 0;
   static const hipError_t attr = [&] {
     hipFuncAttributes fa;
@@ -398,15 +461,30 @@ static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
                                (int)(LDS_PER_CU - static_lds));
   }();
   if (attr != hipSuccess) return attr;
-  // three slots per wave where the LDS allows (the prefix table grows with B)
   const size_t pre = prefix_bytes(a.B);
-  const size_t slots3 = (size_t)WAVES * 3 * mfma_tile_bytes<H>();
-  const int nslots = static_lds + pre + slots3 <= (size_t)LDS_PER_CU ? 3 : 2;
-  const size_t shmem = pre + (size_t)WAVES * nslots * mfma_tile_bytes<H>();
-  if (static_lds + shmem > (size_t)LDS_PER_CU) return hipErrorInvalidConfiguration;
+  int nslots = 2;
+  size_t shmem;
+  if constexpr (QLDS) {
+    shmem = pre + (size_t)NB * 16 * H * 2 + (size_t)WAVES * 2 * mfma_tile_bytes<H>();
+    if (static_lds + shmem > (size_t)LDS_PER_CU / 2) return hipErrorInvalidConfiguration;
+  } else {
+    // three slots per wave where the LDS allows (the prefix table grows with B)
+    const size_t slots3 = (size_t)WAVES * 3 * mfma_tile_bytes<H>();
+    nslots = static_lds + pre + slots3 <= (size_t)LDS_PER_CU ? 3 : 2;
+    shmem = pre + (size_t)WAVES * nslots * mfma_tile_bytes<H>();
+    if (static_lds + shmem > (size_t)LDS_PER_CU) return hipErrorInvalidConfiguration;
+  }
   // one worker per workgroup
   hipLaunchKernelGGL(kern, dim3(a.W), dim3(THREADS), shmem, stream, a, nslots);
   return hipGetLastError();
+}
+
+template <bool BF, int H, int NB, bool PAGED, bool MASKED>
+static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
+  if constexpr (H == 128 && NB <= 3) {
+    if (mfma_two_per_cu(a.B, H, NB * 16)) return launch_mfma_q<BF, H, NB, PAGED, MASKED, true>(a, stream);
+  }
+  return launch_mfma_q<BF, H, NB, PAGED, MASKED, false>(a, stream);
 }
 
 template <bool BF, int H, bool PAGED, bool MASKED>
@@ -434,6 +512,10 @@ static hipError_t launch_mfma_m(const AttnArgs& a, bool bf16, int H, bool paged,
                  : launch_mfma_nb<false, 64, false, MASKED>(a, stream);
   return paged ? launch_mfma_nb<false, 128, true, MASKED>(a, stream)
                : launch_mfma_nb<false, 128, false, MASKED>(a, stream);
+}
+
+int mfma_workgroups_per_cu(int B, int H, int RMAX) {
+  return H == 128 && mfma_two_per_cu(B, H, RMAX) ? 2 : 1;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {

@@ -102,13 +102,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // Bad-entry flags of the segment computed and of the next one (the copies
   // run one step ahead), indexed by segment ordinal parity.
   bool bad2[2] = {false, false};
-  auto issue_k = [&](const StepCursor& c) {
+  auto issue_k = [&](const StepCursor& c) __attribute__((always_inline)) {
     bool bad = false;
     copy_tile<H, PAGED, MASKED>(a, c.s, c.kb, c.tok0, ring_lds, lane, swz, lvoff, bad);
     dma16(a.q + row_index(a, c.s.b, c.s.k, 0) * ROWB, qoff, ring_lds + TILEB);
     bad2[c.ord & 1] |= bad;
   };
-  auto issue_v = [&](const StepCursor& c) {
+  auto issue_v = [&](const StepCursor& c) __attribute__((always_inline)) {
     bool bad = false;
     copy_tile<H, PAGED, MASKED>(a, c.s, c.vb, c.tok0, ring_lds + VSLOT, lane, swz, lvoff, bad);
     bad2[c.ord & 1] |= bad;
@@ -297,7 +297,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (cs.x + 1 >= part.hi) break;
     cs.advance(a, s_pre, part);
   }
-  count_and_merge<H>(a, shared, s_flag);
+  // every copy has landed and every slot has been read: the slots are free
+  __syncthreads();
+  count_and_merge<H>(a, shared, s_flag,
+                     reinterpret_cast<float*>(reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B)),
+                     valu_ring_bytes<H>() / 4);
 }
 
 // ---------------------------------------------------------------- launch

@@ -580,50 +580,117 @@ __device__ __forceinline__ bool count_partial(const AttnArgs& a, const Segment& 
 // Merge all partials of the unit and write the output; called by the
 // workgroup that counted the last one. Every other partial was acknowledged
 // before its count, which preceded ours; device-coherent loads see them. The
-// partials are folded in chunks of 8 whose loads are issued together (one
-// memory round trip per chunk), with an online rescale between chunks. The
 // count is reset for the next call.
+//
+// With LDS scratch for every partial's row statistics (n * rows * 2 floats
+// within `cap`), the merge takes two memory round trips: the statistics of
+// all partials at once (each row's weights computed once, into the scratch),
+// then the outputs, each thread keeping 4 elements x 8 partials of loads in
+// flight. Otherwise the partials are folded in chunks of 8 whose loads are
+// issued together, with an online rescale between chunks.
 template <int H>
-__device__ void merge_partials(const AttnArgs& a, const Segment& s) {
+__device__ void merge_partials(const AttnArgs& a, const Segment& s, float* scratch, int cap) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const int row0 = s.rb * a.RMAX;
   constexpr int CH = 8;
   const int n = s.n_parts;
-#pragma unroll 2
-  for (int e = threadIdx.x; e < rows * H; e += THREADS) {
-    const int r = e / H, h = e - (e / H) * H;
-    float M = NEG_BIG, L = 0.f, O = 0.f;
-    for (int base = 0; base < n; base += CH) {
-      float mi[CH], li[CH], oi[CH];
+  auto slot_of = [&](int j) { return (int64_t)s.first_wg + j + s.unit; };
+  if (n * rows * 2 + 2 * rows <= cap) {
+    float* sw = scratch;                // [n][rows]: m, then the weight 2^(m - M)
+    float* sl = scratch + n * rows;     // [n][rows]: l
+    float* sM = scratch + 2 * n * rows; // [rows]: M, then 1 / L... (M and L)
+    float* sL = sM + rows;
+    for (int e = threadIdx.x; e < n * rows; e += THREADS) {
+      const int j = e / rows, r = e - (e / rows) * rows;
+      const float* ml = a.part_ml + slot_of(j) * a.RMAX * 2 + r * 2;
+      sw[e] = load_coherent(ml);
+      sl[e] = load_coherent(ml + 1);
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < rows; r += THREADS) {
+      float M = NEG_BIG;
+      for (int j = 0; j < n; ++j) M = fmaxf(M, sw[j * rows + r]);
+      float L = 0.f;
+      for (int j = 0; j < n; ++j) {
+        const float w = __builtin_amdgcn_exp2f(sw[j * rows + r] - M);
+        sw[j * rows + r] = w;
+        L += w * sl[j * rows + r];
+      }
+      sM[r] = M;
+      sL[r] = L;
+    }
+    __syncthreads();
+    constexpr int EU = 4;  // elements per thread in flight
+    for (int e0 = threadIdx.x; e0 < rows * H; e0 += THREADS * EU) {
+      float O[EU] = {0.f, 0.f, 0.f, 0.f};
+      for (int jb = 0; jb < n; jb += CH) {
+        float o[EU][CH];
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const bool ok = base + j < n;
-        const int64_t sl = ok ? (int64_t)s.first_wg + base + j + s.unit : (int64_t)s.first_wg + s.unit;
-        const float* ml = a.part_ml + sl * a.RMAX * 2 + r * 2;
-        mi[j] = load_coherent(ml);
-        li[j] = load_coherent(ml + 1);
-        oi[j] = load_coherent(a.part_o + (sl * a.RMAX + r) * H + h);
-        if (!ok) {
-          mi[j] = NEG_BIG;
-          li[j] = 0.f;
-          oi[j] = 0.f;
+        for (int u = 0; u < EU; ++u) {
+          const int e = min(e0 + u * THREADS, rows * H - 1);
+          const int r = e / H, h = e - (e / H) * H;
+#pragma unroll
+          for (int j = 0; j < CH; ++j) {
+            const int jj = min(jb + j, n - 1);
+            o[u][j] = load_coherent(a.part_o + (slot_of(jj) * a.RMAX + r) * H + h);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < EU; ++u) {
+          const int e = min(e0 + u * THREADS, rows * H - 1);
+          const int r = e / H;
+#pragma unroll
+          for (int j = 0; j < CH; ++j)
+            if (jb + j < n) O[u] += sw[(jb + j) * rows + r] * o[u][j];
         }
       }
-      float Mc = M;
 #pragma unroll
-      for (int j = 0; j < CH; ++j) Mc = fmaxf(Mc, mi[j]);
-      const float keep = exp2f(M - Mc);
-      L *= keep;
-      O *= keep;
-      M = Mc;
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const float w = exp2f(mi[j] - M);
-        L += w * li[j];
-        O += w * oi[j];
+      for (int u = 0; u < EU; ++u) {
+        const int e = e0 + u * THREADS;
+        if (e < rows * H) {
+          const int r = e / H, h = e - (e / H) * H;
+          write_final(a, s.b, s.k, row0 + r, H, h, O[u], sM[r], sL[r]);
+        }
       }
     }
-    write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
+    __syncthreads();  // the scratch may be reused
+  } else {
+#pragma unroll 2
+    for (int e = threadIdx.x; e < rows * H; e += THREADS) {
+      const int r = e / H, h = e - (e / H) * H;
+      float M = NEG_BIG, L = 0.f, O = 0.f;
+      for (int base = 0; base < n; base += CH) {
+        float mi[CH], li[CH], oi[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const bool ok = base + j < n;
+          const int64_t sl = ok ? slot_of(base + j) : slot_of(0);
+          const float* ml = a.part_ml + sl * a.RMAX * 2 + r * 2;
+          mi[j] = load_coherent(ml);
+          li[j] = load_coherent(ml + 1);
+          oi[j] = load_coherent(a.part_o + (sl * a.RMAX + r) * H + h);
+          if (!ok) {
+            mi[j] = NEG_BIG;
+            li[j] = 0.f;
+            oi[j] = 0.f;
+          }
+        }
+        float Mc = M;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) Mc = fmaxf(Mc, mi[j]);
+        const float keep = exp2f(M - Mc);
+        L *= keep;
+        O *= keep;
+        M = Mc;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const float w = exp2f(mi[j] - M);
+          L += w * li[j];
+          O += w * oi[j];
+        }
+      }
+      write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
+    }
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.counters[s.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -658,8 +725,10 @@ __device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, 
 // At the end of a worker's range: once its partial stores are acknowledged,
 // count them, then merge every unit whose last partial this worker counted.
 // Needs s_flag[2] in LDS.
+// scratch: LDS free at this point, `cap` floats.
 template <int H>
-__device__ void count_and_merge(const AttnArgs& a, const SharedUnits& sh, int32_t* s_flag) {
+__device__ void count_and_merge(const AttnArgs& a, const SharedUnits& sh, int32_t* s_flag,
+                                float* scratch, int cap) {
   if (sh.n == 0) return;
   wait_stores();
   __syncthreads();
@@ -670,8 +739,8 @@ __device__ void count_and_merge(const AttnArgs& a, const SharedUnits& sh, int32_
     s_flag[1] = f1;
   }
   __syncthreads();
-  if (s_flag[0]) merge_partials<H>(a, sh.s0);
-  if (s_flag[1]) merge_partials<H>(a, sh.s1);
+  if (s_flag[0]) merge_partials<H>(a, sh.s0, scratch, cap);
+  if (s_flag[1]) merge_partials<H>(a, sh.s1, scratch, cap);
 }
 
 }  // namespace kvc
