@@ -63,6 +63,7 @@ struct Plan {
   bool mfma;
   int R, RB, RMAX, units;
   int W;        // workgroups launched
+  int fast;     // workers given the larger share (see Partition), 0: equal shares
   int workers;  // independent workers: waves (vector-ALU kernel) or workgroups (matrix cores)
   size_t off_o, off_ml, bytes;
 };
@@ -88,11 +89,14 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
   if (units > COUNTER_SLOTS) return false;
   p->units = (int)units;
   const int per_wg = 1;  // both kernels: one worker per workgroup
+  p->fast = 0;
   if (num_wg > 0) {
     p->W = num_wg > (1 << 20) ? (1 << 20) : num_wg;
   } else {
     const int64_t steps_ub = units * ((max_seq_len + kvc::STEP - 1) / kvc::STEP);
-    const int64_t full = (int64_t)device_cu_count() * (p->mfma ? kvc::mfma_workgroups_per_cu(B, H, p->RMAX) : kvc::valu_workgroups_per_cu(B, H));
+    const int cus = device_cu_count();
+    const int per_cu = p->mfma ? kvc::mfma_workgroups_per_cu(B, H, p->RMAX) : kvc::valu_workgroups_per_cu(B, H);
+    const int64_t full = (int64_t)cus * per_cu;
     const int64_t unit_steps = (max_seq_len + kvc::STEP - 1) / kvc::STEP;
     int64_t want_workers = unit_steps <= SHORT_UNIT_STEPS
                                ? units
@@ -101,6 +105,9 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
     int64_t want = (want_workers + per_wg - 1) / per_wg;
     if (want > full) want = full;
     p->W = (int)(want < 1 ? 1 : want);
+    // two per CU and a full round: the first `cus` workgroups are each the
+    // older of a CU's pair
+    p->fast = per_cu == 2 && p->W == full ? cus : 0;
   }
   p->workers = p->W * per_wg;
   const size_t slots = (size_t)p->workers + (size_t)p->units;
@@ -228,6 +235,7 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   a.RMAX = p.RMAX;
   a.out_dtype = out_dtype;
   a.W = p.workers;
+  a.fast_workers = p.fast;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.window = window;
   a.tree = tree;

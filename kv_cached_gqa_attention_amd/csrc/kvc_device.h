@@ -64,6 +64,7 @@ struct AttnArgs {
   int32_t RMAX;  // rows per row block (the last block may be partial)
   int32_t out_dtype;  // 0 f16, 1 bf16, 2 f32
   int32_t W;          // workers sharing the tiles (waves or workgroups, per kernel)
+  int32_t fast_workers;  // the first fast_workers get the larger share (0: equal shares)
   float scale_log2;   // scale * log2(e)
   float* part_o;      // [W + units, RMAX, H], slot = worker + unit
   float* part_ml;     // [W + units, RMAX, 2]
@@ -330,14 +331,35 @@ struct Segment {
   int first_wg;   // first worker sharing the unit
 };
 
+// Workers' shares of the steps: equal, or (fast > 0) weighted FAST_SHARE :
+// SLOW_SHARE between the first `fast` workers and the rest. With two
+// workgroups per CU the hardware places workgroup i and i + (number of CUs)
+// on one CU, and the older of the two is served first (about 25% faster);
+// weighting the shares lets both finish together.
+constexpr int FAST_SHARE = 5, SLOW_SHARE = 4;
+
 struct Partition {
   int64_t total;  // steps over all units
   int w_eff;      // workers with work: min(W, total); each then has >= 1 step
   int64_t lo, hi; // this worker's flat step range
   int krb;        // K * RB
+  int fast;       // workers with the larger share (0: equal shares)
+  int64_t wt;     // sum of the shares (w_eff when equal)
 
+  __device__ int64_t share_prefix(int w) const {  // shares of workers [0, w)
+    if (!fast) return w;
+    return w <= fast ? (int64_t)FAST_SHARE * w
+                     : (int64_t)FAST_SHARE * fast + (int64_t)SLOW_SHARE * (w - fast);
+  }
+  // Worker w's range is [total * P(w) / wt, total * P(w + 1) / wt), P the
+  // share prefix; the owner of step x is the largest w with P(w) <= u.
   __device__ int owner(int64_t x) const {  // worker whose range holds step x
-    return (int)(((x + 1) * (int64_t)w_eff - 1) / total);
+    const int64_t u = ((x + 1) * wt - 1) / total;
+    if (!fast) return (int)u;
+    const int64_t w = u < (int64_t)FAST_SHARE * fast
+                          ? u / FAST_SHARE
+                          : fast + (u - (int64_t)FAST_SHARE * fast) / SLOW_SHARE;
+    return (int)(w < w_eff - 1 ? w : w_eff - 1);
   }
 };
 
@@ -347,9 +369,14 @@ __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int
   p.krb = a.K * a.RB;
   p.total = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[a.B]) * p.krb;
   p.w_eff = (int)(p.total < (int64_t)a.W ? p.total : (int64_t)a.W);
+  // weighted only with at least two steps per worker, so every share keeps
+  // at least one step (4 / 5 of 2 rounds down to 1)
+  p.fast = a.fast_workers > 0 && a.fast_workers < p.w_eff && p.total >= 2 * (int64_t)p.w_eff
+               ? a.fast_workers : 0;
+  p.wt = p.share_prefix(p.w_eff);
   if (w < p.w_eff) {
-    p.lo = (int64_t)w * p.total / p.w_eff;
-    p.hi = (int64_t)(w + 1) * p.total / p.w_eff;
+    p.lo = p.total * p.share_prefix(w) / p.wt;
+    p.hi = p.total * p.share_prefix(w + 1) / p.wt;
   } else {
     p.lo = p.hi = 0;
   }
