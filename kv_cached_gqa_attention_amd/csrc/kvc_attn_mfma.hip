@@ -441,7 +441,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   }
   // every copy has landed and every slot has been read: the slots are free
   __syncthreads();
-  count_and_merge<H>(a, shared, s_flag, reinterpret_cast<float*>(ring_all),
+  count_and_merge<H, (RMAX * H + THREADS - 1) / THREADS>(a, shared, s_flag, reinterpret_cast<float*>(ring_all),
                      WAVES * nslots * TILEB / 4);
 }
 

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   // every copy has landed and every slot has been read: the slots are free
   __syncthreads();
-  count_and_merge<H>(a, shared, s_flag,
+  count_and_merge<H, (R * H + THREADS - 1) / THREADS>(a, shared, s_flag,
                      reinterpret_cast<float*>(reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B)),
                      valu_ring_bytes<H>() / 4);
 }

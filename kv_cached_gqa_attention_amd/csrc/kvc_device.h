@@ -280,7 +280,7 @@ __device__ __forceinline__ bool key_visible(const AttnArgs& a, int tok, int new0
 // unit loop would be waited for together with the tile prefetches).
 // s_pre holds 2B + 1 ints. Requires THREADS threads and a scratch of WAVES
 // ints.
-__device__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_wave) {
+__device__ __forceinline__ void build_tile_prefix(const AttnArgs& a, int32_t* s_pre, int32_t* s_wave) {
   const int tid = threadIdx.x;
   const int per = (a.B + THREADS - 1) / THREADS;
   const int b0 = tid * per;
@@ -429,7 +429,7 @@ __device__ __forceinline__ Segment find_segment(const AttnArgs& a, const int32_t
 // see them and no other workgroup reads them. Requires one row block per
 // (b, k): with several, other workgroups would read the rows too.
 template <int H, int NT, bool PAGED>
-__device__ void append_owned(const AttnArgs& a, const int32_t* s_pre, const Partition& part) {
+__device__ __forceinline__ void append_owned(const AttnArgs& a, const int32_t* s_pre, const Partition& part) {
   if (!a.k_new) return;
   constexpr int CPR = H / 8;  // 16-byte chunks per row
   for (int64_t x = part.lo; x < part.hi;) {
@@ -479,7 +479,7 @@ __device__ __forceinline__ void write_final(const AttnArgs& a, int b, int k, int
 // NaN outputs for the rows of sequences with an invalid length. Units are
 // dealt round-robin to all launched workgroups.
 template <int H>
-__device__ void fill_invalid(const AttnArgs& a) {
+__device__ __forceinline__ void fill_invalid(const AttnArgs& a) {
   const float qnan = __int_as_float(0x7fc00000);
   const int units = a.B * a.K;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
@@ -553,7 +553,7 @@ __device__ __forceinline__ void combine_waves(const AttnArgs& a, const float* s_
 // The segment is its whole unit: write the output. Ends with a barrier, so
 // LDS may be reused afterwards.
 template <int H, int NW>
-__device__ void finish_direct(const AttnArgs& a, const Segment& s, const float* s_m,
+__device__ __forceinline__ void finish_direct(const AttnArgs& a, const Segment& s, const float* s_m,
                               const float* s_l, const float* s_o, float* s_w, bool bad) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const int row0 = s.rb * a.RMAX;
@@ -574,7 +574,7 @@ __device__ void finish_direct(const AttnArgs& a, const Segment& s, const float* 
 // before the partial is counted. Ends with a barrier, so LDS may be reused
 // afterwards.
 template <int H, int NW>
-__device__ void store_partial(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
+__device__ __forceinline__ void store_partial(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
                               const float* s_l, const float* s_o, float* s_w, bool bad) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const float qnan = __int_as_float(0x7fc00000);
@@ -610,19 +610,20 @@ __device__ __forceinline__ bool count_partial(const AttnArgs& a, const Segment& 
 // count is reset for the next call.
 //
 // With LDS scratch for every partial's row statistics (n * rows * 2 floats
-// within `cap`), the merge takes two memory round trips: the statistics of
-// all partials at once (each row's weights computed once, into the scratch),
-// then the outputs, each thread keeping 4 elements x 8 partials of loads in
-// flight. Otherwise the partials are folded in chunks of 8 whose loads are
-// issued together, with an online rescale between chunks.
-template <int H>
-__device__ void merge_partials(const AttnArgs& a, const Segment& s, float* scratch, int cap) {
+// within `cap`) and rows * H <= EPT * THREADS, the merge takes 1 + n memory
+// round trips: the statistics of all partials at once (each row's weights
+// computed once, into the scratch), then per partial one load for each of
+// the thread's EPT output elements, all in flight together. Otherwise the
+// partials are folded in chunks of 8 whose loads are issued together, with
+// an online rescale between chunks.
+template <int H, int EPT>
+__device__ __forceinline__ void merge_partials(const AttnArgs& a, const Segment& s, float* scratch, int cap) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const int row0 = s.rb * a.RMAX;
   constexpr int CH = 8;
   const int n = s.n_parts;
   auto slot_of = [&](int j) { return (int64_t)s.first_wg + j + s.unit; };
-  if (n * rows * 2 + 2 * rows <= cap) {
+  if (n * rows * 2 + 2 * rows <= cap && rows * H <= EPT * THREADS) {
     float* sw = scratch;                // [n][rows]: m, then the weight 2^(m - M)
     float* sl = scratch + n * rows;     // [n][rows]: l
     float* sM = scratch + 2 * n * rows; // [rows]: M, then 1 / L... (M and L)
@@ -647,34 +648,32 @@ __device__ void merge_partials(const AttnArgs& a, const Segment& s, float* scrat
       sL[r] = L;
     }
     __syncthreads();
-    constexpr int EU = 4;  // elements per thread in flight
-    for (int e0 = threadIdx.x; e0 < rows * H; e0 += THREADS * EU) {
-      float O[EU] = {0.f, 0.f, 0.f, 0.f};
-      for (int jb = 0; jb < n; jb += CH) {
-        float o[EU][CH];
+    // each thread's EPT elements in passes of up to 16, one partial at a
+    // time: per partial, a pass's loads are all in flight together
+    constexpr int EP = EPT < 16 ? EPT : 16;
 #pragma unroll
-        for (int u = 0; u < EU; ++u) {
-          const int e = min(e0 + u * THREADS, rows * H - 1);
-          const int r = e / H, h = e - (e / H) * H;
+    for (int p0 = 0; p0 < EPT; p0 += EP) {
+      float O[EP];
 #pragma unroll
-          for (int j = 0; j < CH; ++j) {
-            const int jj = min(jb + j, n - 1);
-            o[u][j] = load_coherent(a.part_o + (slot_of(jj) * a.RMAX + r) * H + h);
-          }
+      for (int u = 0; u < EP; ++u) O[u] = 0.f;
+      for (int j = 0; j < n; ++j) {
+        const float* po = a.part_o + slot_of(j) * a.RMAX * H;
+        float o[EP];
+#pragma unroll
+        for (int u = 0; u < EP; ++u) {
+          const int e = min((int)threadIdx.x + (p0 + u) * THREADS, rows * H - 1);
+          o[u] = load_coherent(po + e);
         }
 #pragma unroll
-        for (int u = 0; u < EU; ++u) {
-          const int e = min(e0 + u * THREADS, rows * H - 1);
-          const int r = e / H;
-#pragma unroll
-          for (int j = 0; j < CH; ++j)
-            if (jb + j < n) O[u] += sw[(jb + j) * rows + r] * o[u][j];
+        for (int u = 0; u < EP; ++u) {
+          const int e = min((int)threadIdx.x + (p0 + u) * THREADS, rows * H - 1);
+          O[u] += sw[j * rows + e / H] * o[u];
         }
       }
 #pragma unroll
-      for (int u = 0; u < EU; ++u) {
-        const int e = e0 + u * THREADS;
-        if (e < rows * H) {
+      for (int u = 0; u < EP; ++u) {
+        const int e = threadIdx.x + (p0 + u) * THREADS;
+        if (p0 + u < EPT && e < rows * H) {
           const int r = e / H, h = e - (e / H) * H;
           write_final(a, s.b, s.k, row0 + r, H, h, O[u], sM[r], sL[r]);
         }
@@ -738,7 +737,7 @@ struct SharedUnits {
 // Finish a segment: the output, or a partial to be counted at the worker's
 // end. Ends with a barrier, so LDS may be reused afterwards.
 template <int H, int NW>
-__device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
+__device__ __forceinline__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
                                const float* s_l, const float* s_o, float* s_w, bool bad,
                                SharedUnits& sh) {
   if (s.n_parts == 1) {
@@ -752,9 +751,10 @@ __device__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, 
 // At the end of a worker's range: once its partial stores are acknowledged,
 // count them, then merge every unit whose last partial this worker counted.
 // Needs s_flag[2] in LDS.
-// scratch: LDS free at this point, `cap` floats.
-template <int H>
-__device__ void count_and_merge(const AttnArgs& a, const SharedUnits& sh, int32_t* s_flag,
+// scratch: LDS free at this point, `cap` floats; EPT: output elements per
+// thread of a merge (rows per unit * H / THREADS, rounded up).
+template <int H, int EPT>
+__device__ __forceinline__ void count_and_merge(const AttnArgs& a, const SharedUnits& sh, int32_t* s_flag,
                                 float* scratch, int cap) {
   if (sh.n == 0) return;
   wait_stores();
@@ -766,8 +766,8 @@ __device__ void count_and_merge(const AttnArgs& a, const SharedUnits& sh, int32_
     s_flag[1] = f1;
   }
   __syncthreads();
-  if (s_flag[0]) merge_partials<H>(a, sh.s0, scratch, cap);
-  if (s_flag[1]) merge_partials<H>(a, sh.s1, scratch, cap);
+  if (s_flag[0]) merge_partials<H, EPT>(a, sh.s0, scratch, cap);
+  if (s_flag[1]) merge_partials<H, EPT>(a, sh.s1, scratch, cap);
 }
 
 }  // namespace kvc

@@ -111,14 +111,14 @@ struct StepCursor {
   const char* vb;
   Segment s;
 
-  __device__ void begin(const AttnArgs& a, const int32_t* s_pre, const Partition& p, int64_t x0,
+  __device__ __forceinline__ void begin(const AttnArgs& a, const int32_t* s_pre, const Partition& p, int64_t x0,
                         int w) {
     x = x0;
     ord = 0;
     wave = w;
     enter(a, s_pre, p);
   }
-  __device__ void advance(const AttnArgs& a, const int32_t* s_pre, const Partition& p) {
+  __device__ __forceinline__ void advance(const AttnArgs& a, const int32_t* s_pre, const Partition& p) {
     ++x;
     tok0 += STEP;
     if (x == end && x < p.hi) {
@@ -128,7 +128,7 @@ struct StepCursor {
   }
 
  private:
-  __device__ void enter(const AttnArgs& a, const int32_t* s_pre, const Partition& p) {
+  __device__ __forceinline__ void enter(const AttnArgs& a, const int32_t* s_pre, const Partition& p) {
     s = find_segment(a, s_pre, p, x);
     end = x + (s.t_end - s.t_begin);
     tok0 = (s.t_begin * WAVES + wave) * TILE;
