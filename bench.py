@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn KV read GB/s (% of ~8 TB/s HBM peak); tokens/s per step"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix cores (MI355X published figure)
 # Infinity Cache (MALL) on MI355X; cache replicas are rotated so that each
 # step's reads exceed it at least twice over.
 MALL_BYTES = 256 << 20
@@ -171,6 +172,20 @@ def profiled_traffic(kernel: str, workload: str):
                     return None
                 return int(rec["fetch_bytes"] + rec["write_bytes"])
     return None
+
+
+def attn_flops(w, seq_lens) -> int:
+    """Algorithmic flops of one step: for every new token and query head,
+    2 H for each visible key's q.k and 2 H for its p.v (causal inside the
+    block; with a window at most W keys; with a draft tree the tree's
+    ancestors among the new tokens, counted as causal here, an upper
+    bound)."""
+    rows = np.asarray(seq_lens, dtype=np.int64)
+    t = np.arange(w.T, dtype=np.int64)
+    vis = rows[:, None] - w.T + t[None, :] + 1  # keys visible to new token t
+    if w.window:
+        vis = np.minimum(vis, w.window)
+    return int(vis.sum()) * w.N * w.H * 4
 
 
 def kv_bytes(w, seq_lens) -> int:
@@ -324,6 +339,10 @@ def main():
     torch.cuda.synchronize()
     attn_ms = e0.elapsed_time(e1) / (args.steps * layers)
     achieved = step_bytes / (attn_ms * 1e-3) / 1e9
+    # bound: the matrix cores where the step's flops per K/V byte exceed their
+    # balance against HBM (a chunk of prefill), else HBM
+    step_flops = attn_flops(w, seq_lens)
+    mfma_bound = step_flops / step_bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     kernel = "attn_mfma_kernel" if w.G * w.T > (8 if w.H == 64 else 4) else "attn_valu_kernel"
     traffic = profiled_traffic(kernel, w.name)
 
@@ -372,6 +391,16 @@ def main():
             "bytes_per_launch": step_bytes,
         },
     }
+    if mfma_bound:
+        tflops = step_flops / (attn_ms * 1e-3) / 1e12
+        result["roofline"].update({
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+            "flops_per_launch": step_flops,
+        })
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(w, prior, w.seed, args.cpu_seconds)

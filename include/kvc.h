@@ -77,6 +77,9 @@ typedef enum { KVC_F16 = 0, KVC_BF16 = 1, KVC_F32 = 2 } kvc_dtype;
  * kvc_attn_decode). */
 #define KVC_WORKSPACE_COUNTERS (1 << 18)
 
+/* Largest number of new tokens per sequence in one attention call. */
+#define KVC_MAX_T 2048
+
 /*
  * One layer's key cache and value cache (same layout, same dtype).
  *
@@ -164,10 +167,18 @@ kvc_status kvc_attn_decode(const kvc_cache *cache, const void *q, void *out, int
                            size_t workspace_bytes, void *stream);
 
 /*
- * Verify: T new query tokens per sequence (1 <= T <= 16), causal inside the
- * block: token t sees the P_b prior keys and new tokens 0 .. t.
+ * Verify: T new query tokens per sequence (1 <= T <= KVC_MAX_T), causal
+ * inside the block: token t sees the P_b prior keys and new tokens 0 .. t.
+ * A short block (T = n + 1 for n drafted tokens) is the speculative verify
+ * pass; a long one is a chunk of prefill against the cache ("CS336, lectures
+ * 10 and 12", section on the two stages of inference: prefill runs the
+ * prompt through the model in one parallel pass and fills the KV cache; its
+ * attention has intensity about S/2, so it is bound by the matrix cores, not
+ * by memory). The new rows must already be in the cache (kvc_append, or use
+ * kvc_append_attend).
  * q: [B, T, N, H]; out: [B, T, N, H]; lse: [B, T, N] fp32 or NULL.
- * Other arguments and errors as kvc_attn_decode (max_seq_len >= T).
+ * Other arguments and errors as kvc_attn_decode (max_seq_len >= T), plus
+ * KVC_ERR_INVALID for T > KVC_MAX_T.
  */
 kvc_status kvc_attn_verify(const kvc_cache *cache, const void *q, void *out, int out_dtype,
                            float *lse, int B, int T, int N, int K, int H, const int32_t *seq_lens,
@@ -218,7 +229,7 @@ kvc_status kvc_append_attend(const kvc_cache *cache, const void *k_new, const vo
  *   with custom attention masks): new token t of sequence b sees new token u
  *   exactly when bit u of tree_mask[b * T + t] is set (set t's own bit and
  *   its ancestors'); every prior row stays visible; bits >= T are ignored.
- *   4-byte aligned. A query that sees no key at all gets NaN.
+ *   4-byte aligned; T <= 32. A query that sees no key at all gets NaN.
  *   Both options compose: a key must pass both rules.
  * k_new, v_new: NULL, or the new rows to append first, as kvc_append_attend.
  * reserved: must be 0.
@@ -237,7 +248,8 @@ typedef struct {
  * NULL). The workspace size from kvc_workspace_bytes for the same B, T, N,
  * K, H, max_seq_len and num_workgroups is always enough (a window only
  * lowers the need). Errors: as kvc_attn_verify and kvc_append_attend, plus
- * KVC_ERR_INVALID for window < 0, reserved != 0 or a misaligned tree_mask.
+ * KVC_ERR_INVALID for window < 0, reserved != 0, a misaligned tree_mask or a
+ * tree_mask with T > 32.
  */
 kvc_status kvc_attn(const kvc_cache *cache, const kvc_attn_options *opts, const void *q, void *out,
                     int out_dtype, float *lse, int B, int T, int N, int K, int H,

@@ -22,6 +22,8 @@ KVC_F16 = 0
 KVC_BF16 = 1
 KVC_F32 = 2
 
+KVC_MAX_T = 2048  # new tokens per sequence in one attention call (include/kvc.h)
+
 # Every symbol the header declares, in declaration order.
 EXPORTS = (
     "kvc_append",

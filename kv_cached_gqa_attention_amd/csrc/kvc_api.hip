@@ -69,7 +69,7 @@ struct Plan {
 };
 
 bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, Plan* p) {
-  if (B < 1 || T < 1 || T > 16 || N < 1 || K < 1 || N % K || (H != 64 && H != 128) ||
+  if (B < 1 || T < 1 || T > KVC_MAX_T || N < 1 || K < 1 || N % K || (H != 64 && H != 128) ||
       max_seq_len < 1 || num_wg < 0 || B > MAX_B)
     return false;
   const int G = N / K;
@@ -187,7 +187,8 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   int capacity = 0, shift = 0;
   const kvc_status st = check_cache(c, K, H, &capacity, &shift);
   if (st != KVC_OK) return st;
-  if (B < 0 || T < 1 || T > 16 || N < 1 || N % K || num_wg < 0) return KVC_ERR_INVALID;
+  if (B < 0 || T < 1 || T > KVC_MAX_T || N < 1 || N % K || num_wg < 0) return KVC_ERR_INVALID;
+  if (tree && T > 32) return KVC_ERR_INVALID;  // one 32-bit mask word per new token
   if (out_dtype != KVC_F16 && out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
   if (max_seq_len < T || max_seq_len > capacity) return KVC_ERR_INVALID;
   if (!isfinite(scale)) return KVC_ERR_INVALID;

@@ -53,11 +53,19 @@ def test_status_strings(lib):
     assert "unknown" in lib.kvc_status_string(7).decode()
 
 
+def test_header_constants_match_the_binding():
+    import re
+
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "kvc.h")).read()
+    assert int(re.search(r"#define KVC_MAX_T (\d+)", hdr).group(1)) == _lib.KVC_MAX_T
+
+
 def test_workspace_bytes(lib):
     assert lib.kvc_workspace_bytes(64, 1, 32, 8, 128, 4097, 0) > 0
     assert lib.kvc_workspace_bytes(64, 1, 32, 8, 96, 4097, 0) == 0  # H
     assert lib.kvc_workspace_bytes(64, 1, 30, 8, 128, 4097, 0) == 0  # N % K
-    assert lib.kvc_workspace_bytes(64, 17, 32, 8, 128, 4097, 0) == 0  # T
+    assert lib.kvc_workspace_bytes(64, 2049, 32, 8, 128, 4097, 0) == 0  # T > KVC_MAX_T
+    assert lib.kvc_workspace_bytes(8, 512, 32, 8, 128, 4097, 0) > 0  # chunked prefill
     assert lib.kvc_workspace_bytes(0, 1, 32, 8, 128, 4097, 0) == 0  # B
     a = lib.kvc_workspace_bytes(8, 5, 64, 8, 128, 9000, 100)
     b = lib.kvc_workspace_bytes(8, 5, 64, 8, 128, 9000, 1000)
@@ -134,7 +142,7 @@ def test_verify_and_append_host_errors(lib):
                                             kw.get("N", 64), 8, 128, FAKE, kw.get("L", 4096), 0.1, 0,
                                             FAKE, 1 << 30, None)
     assert v(0) == E.KVC_ERR_INVALID
-    assert v(17) == E.KVC_ERR_INVALID
+    assert v(2049) == E.KVC_ERR_INVALID  # T > KVC_MAX_T
     assert v(5, L=4) == E.KVC_ERR_INVALID  # max_seq_len < T
     ap = lambda **kw: lib.kvc_append(ctypes.byref(kw.get("c", c)), kw.get("kn", FAKE), FAKE,
                                      kw.get("B", 8), kw.get("T", 1), 8, kw.get("H", 128), FAKE, None)
@@ -165,7 +173,7 @@ def test_append_attend_host_errors(lib):
     assert aa(kn=FAKE + 4) == E.KVC_ERR_INVALID
     assert aa(vn=FAKE + 8) == E.KVC_ERR_INVALID
     assert aa(T=0) == E.KVC_ERR_INVALID
-    assert aa(T=17) == E.KVC_ERR_INVALID
+    assert aa(T=2049) == E.KVC_ERR_INVALID
     assert aa(N=60) == E.KVC_ERR_INVALID
     assert aa(H=80) == E.KVC_ERR_UNSUPPORTED
     assert aa(L=4097) == E.KVC_ERR_INVALID
@@ -194,7 +202,8 @@ def test_attn_options_layout_and_errors(lib):
     assert at(window=-1) == E.KVC_ERR_INVALID
     assert at(reserved=3) == E.KVC_ERR_INVALID
     assert at(tree=FAKE + 2) == E.KVC_ERR_INVALID
-    assert at(T=17) == E.KVC_ERR_INVALID
+    assert at(T=2049) == E.KVC_ERR_INVALID
+    assert at(T=33, tree=FAKE) == E.KVC_ERR_INVALID  # one 32-bit mask word per new token
     assert at(ws=None) == E.KVC_ERR_WORKSPACE
     assert at(B=0) == E.KVC_OK
     assert at(B=0, opts=False) == E.KVC_OK

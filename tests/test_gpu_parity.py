@@ -288,6 +288,38 @@ def test_large_batches(gpu_device, B, T, N, K, H, dtype, layout):
     compare_units(run, units)
 
 
+# ----------------------------------------------------------------- chunks of prefill (large T)
+
+PREFILL = [
+    # B, T, N, K, H, dtype, prior
+    (2, 64, 8, 2, 128, BF, [0, 300]),       # G*T = 256: four row blocks; empty prefix
+    (1, 200, 14, 2, 64, HF, [100]),         # the measured model's heads, 200-token chunk
+    (2, 128, 32, 8, 128, BF, [1000, 37]),   # batched, 128-token chunks
+    (1, 33, 64, 8, 128, BF, [0]),           # a whole 33-token prompt, ragged last row block
+]
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("case", PREFILL, ids=_ids(PREFILL))
+def test_prefill_chunk_matches_oracle(gpu_device, case, layout):
+    """A chunk of T prompt tokens against the cached prefix, causal inside the
+    chunk: every (b, k) against the oracle."""
+    B, T, N, K, H, dtype, prior = case
+    run = run_case(B, T, N, K, H, dtype, prior, layout=layout, seed=300 + T)
+    compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("case", [PREFILL[0], PREFILL[2]], ids=_ids([PREFILL[0], PREFILL[2]]))
+def test_prefill_chunk_fused_and_any_workgroup_count(gpu_device, case):
+    """The fused entry point (the append runs as its own launch when a
+    (b, k) spans several row blocks) and explicit grids of 1, 7 and 5000
+    workgroups all give the oracle's result."""
+    B, T, N, K, H, dtype, prior = case
+    for nwg, fused in [(0, True), (1, False), (7, True), (5000, False)]:
+        run = run_case(B, T, N, K, H, dtype, prior, seed=310, num_workgroups=nwg, fused=fused)
+        compare_units(run, all_units(run.inp))
+
+
 # ----------------------------------------------------------------- fused append + attend
 
 FUSED = [SMALL[0], SMALL[3], SMALL[5], SMALL[7], SMALL[9], SMALL[11], SMALL[12], SMALL[13]]

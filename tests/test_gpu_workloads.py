@@ -1,4 +1,4 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration
+"""GPU parity at the workloads' full sizes, in the launch configuration
 the bench times (automatic workgroup count). Where the oracle would take too
 long on every unit, a seeded sample of (sequence, key-value head) units is
 checked; each sampled unit is checked on every query row and every dim.
@@ -117,5 +117,15 @@ def test_tree_verify_b32_t8_sampled(gpu_device):
                    draw_device=gpu_device, tree=words)
     rng = np.random.default_rng(w.seed)
     units = [(int(b), int(rng.integers(0, w.K))) for b in rng.permutation(w.B)[:24]]
+    compare_units(run, units)
+    assert torch.isfinite(run.out).all()
+
+
+def test_prefill_chunk_b8_t512_sampled(gpu_device):
+    w = WORKLOADS["prefill_chunk_b8_t512"]
+    run = run_case(w.B, w.T, w.N, w.K, w.H, w.dtype, _prior(w), layout=w.layout, seed=w.seed,
+                   draw_device=gpu_device)
+    rng = np.random.default_rng(w.seed)
+    units = [(int(b), int(rng.integers(0, w.K))) for b in rng.permutation(w.B)[:4]]
     compare_units(run, units)
     assert torch.isfinite(run.out).all()

@@ -224,11 +224,13 @@ def test_mha_equals_independent_heads():
 # --------------------------------------------------------------------------- cached == recompute
 
 
-@pytest.mark.parametrize("T", [1, 3, 5])
+@pytest.mark.parametrize("T", [1, 3, 5, 20, 37])
 @pytest.mark.parametrize("N,K", [(6, 2), (4, 4), (4, 1)])
 def test_cached_equals_full_causal_recompute(T, N, K):
     """Caching is exact: the last T rows of the uncached, masked n x n recompute
-    equal the cached oracle over the first L - T rows plus the T new ones."""
+    equal the cached oracle over the first L - T rows plus the T new ones
+    (T = 20: a chunk of prefill against a 17-row prefix; T = L: the whole
+    prompt against an empty cache)."""
     rng = np.random.default_rng(100 + 10 * T + N + K)
     L, H = 37, 16
     q_all = rng.standard_normal((L, N, H))

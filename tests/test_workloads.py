@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 import torch
 
+from kv_cached_gqa_attention_amd import _lib
 from workloads import (
     WORKLOADS,
     draw_inputs,
@@ -82,7 +83,7 @@ def test_paged_layout_round_trips_through_the_table():
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
 def test_workload_shapes(name):
     w = WORKLOADS[name]
-    assert w.N % w.K == 0 and w.H in (64, 128) and 1 <= w.T <= 16
+    assert w.N % w.K == 0 and w.H in (64, 128) and 1 <= w.T <= _lib.KVC_MAX_T
     assert w.dtype in (torch.float16, torch.bfloat16)
     assert w.window >= 0
     if w.tree_parents:

@@ -20,7 +20,11 @@ Shapes follow the pages on KV-cached inference:
 * a draft tree of 8 tokens verified in one pass ("Accelerating Sonar through
   speculation", section "EAGLE": top-k branches at each node; the shape
   here, a root with two children and two grandchildren each plus one more
-  level, is a reading).
+  level, is a reading);
+* a 512-token chunk of prefill against a cached prefix ("CS336, lectures 10
+  and 12", section on the two stages of inference: prefill runs the prompt
+  in one parallel pass and fills the cache; chunking a long prompt and the
+  512-token chunk are a reading, the pages give no chunk size).
 
 "Context" in each description is the PRIOR cached context P_b; the T new
 tokens are appended on top of it, so a sequence attends over P_b + T keys.
@@ -117,6 +121,13 @@ WORKLOADS = {
         B=32, N=64, K=8, H=128, T=8, dtype=torch.bfloat16,
         prior_lo=2048, prior_hi=8192, layout="contiguous", seed=SEED_BASE + 7,
         tree_parents=(-1, 0, 0, 1, 1, 2, 2, 3),
+    ),
+    "prefill_chunk_b8_t512": Workload(
+        name="prefill_chunk_b8_t512",
+        description="B=8, N=32, K=8, H=128, bf16, T=512 prompt tokens per sequence (a chunk of "
+                    "prefill, causal inside the chunk), cached prefix U[1024,4096], contiguous",
+        B=8, N=32, K=8, H=128, T=512, dtype=torch.bfloat16,
+        prior_lo=1024, prior_hi=4096, layout="contiguous", seed=SEED_BASE + 8,
     ),
 }
 
