@@ -158,7 +158,9 @@ kvc_status kvc_append(const kvc_cache *cache, const void *k_new, const void *v_n
  * that overlap in time must not share a workspace.
  * Errors: as kvc_append, plus KVC_ERR_INVALID for N < 1, N % K != 0,
  * max_seq_len out of range; KVC_ERR_UNSUPPORTED for B > 4096 or more than
- * KVC_WORKSPACE_COUNTERS units (B * K * ceil(G * T / 64)); KVC_ERR_WORKSPACE
+ * KVC_WORKSPACE_COUNTERS units (B * K * row blocks, a row block holding up to
+ * 64 of the G * T query rows of a (b, k), 48 when there are more than 64);
+ * KVC_ERR_WORKSPACE
  * for a missing, misaligned or small workspace.
  */
 kvc_status kvc_attn_decode(const kvc_cache *cache, const void *q, void *out, int out_dtype,

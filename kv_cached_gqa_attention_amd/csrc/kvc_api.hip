@@ -68,6 +68,16 @@ struct Plan {
   size_t off_o, off_ml, bytes;
 };
 
+// Query-row blocks per (b, k) on the matrix cores for R rows: one block of
+// up to 64 rows; long query blocks (several row blocks anyway) take blocks of
+// at most 48 rows, whose matrix-core form runs two workgroups per CU where
+// the LDS allows (each further row block re-reads the unit's K/V rows).
+int row_blocks(int R, int H) {
+  const int nb_total = (R + 15) / 16;
+  const int max_nb = nb_total > MFMA_MAX_NB && H == 128 ? 3 : MFMA_MAX_NB;
+  return (nb_total + max_nb - 1) / max_nb;
+}
+
 bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, Plan* p) {
   if (B < 1 || T < 1 || T > KVC_MAX_T || N < 1 || K < 1 || N % K || (H != 64 && H != 128) ||
       max_seq_len < 1 || num_wg < 0 || B > MAX_B)
@@ -81,7 +91,7 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
   } else {
     p->mfma = true;
     const int nb_total = (p->R + 15) / 16;
-    p->RB = (nb_total + MFMA_MAX_NB - 1) / MFMA_MAX_NB;
+    p->RB = row_blocks(p->R, H);
     const int nb = (nb_total + p->RB - 1) / p->RB;
     p->RMAX = nb * 16;
   }
@@ -198,7 +208,8 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   if (!aligned16(q) || !aligned16(out)) return KVC_ERR_INVALID;
   const bool fused = k_new != nullptr || v_new != nullptr;
   if (fused && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return KVC_ERR_INVALID;
-  if ((int64_t)B * K * ((N / K * T + 63) / 64) > COUNTER_SLOTS) return KVC_ERR_UNSUPPORTED;
+  if ((int64_t)B * K * (N / K * T <= valu_max_rows(H) ? 1 : row_blocks(N / K * T, H)) > COUNTER_SLOTS)
+    return KVC_ERR_UNSUPPORTED;
   // a window bounds the keys any call streams per unit: at most
   // window + T - 1 positions, starting anywhere inside a 128-token step
   int span = max_seq_len;
