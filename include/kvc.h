@@ -159,7 +159,7 @@ kvc_status kvc_append(const kvc_cache *cache, const void *k_new, const void *v_n
  * Errors: as kvc_append, plus KVC_ERR_INVALID for N < 1, N % K != 0,
  * max_seq_len out of range; KVC_ERR_UNSUPPORTED for B > 4096 or more than
  * KVC_WORKSPACE_COUNTERS units (B * K * row blocks, a row block holding up to
- * 64 of the G * T query rows of a (b, k), 48 when there are more than 64);
+ * 64 of the G * T query rows of a (b, k), 128 when there are more than 64);
  * KVC_ERR_WORKSPACE
  * for a missing, misaligned or small workspace.
  */
@@ -195,7 +195,7 @@ kvc_status kvc_attn_verify(const kvc_cache *cache, const void *q, void *out, int
  * ("Making inference cheap: KV cache, batching and quantization": each step
  * extends the cache by the new token's rows and attends over the whole
  * cache). It saves the separate append launch: when every (b, k) is served
- * by one row block (G * T <= 64, true for all decode and short verify
+ * by one row block (G * T <= 128, true for all decode and short verify
  * shapes) the append happens inside the attention kernel, each new row
  * written by the workgroup that later reads it; otherwise the call enqueues
  * the append kernel and then the attention kernel.

@@ -34,49 +34,60 @@ constexpr int MIN_STEPS_PER_WORKER = 2;
 // kernel's register and LDS use lets reside (valu_workgroups_per_cu,
 // mfma_workgroups_per_cu).
 constexpr int DEFAULT_CUS = 256;
+constexpr int DEFAULT_XCDS = 8;
 // The workspace starts with a fixed-size array of per-unit counters. Only the
 // counter atomics (and their reset to zero by the merging workgroup) ever
 // write it, so it stays zero between calls whatever shapes they have; the
 // partials that follow are scratch, always written before being read.
 constexpr int64_t COUNTER_SLOTS = KVC_WORKSPACE_COUNTERS;
 
-int device_cu_count() {
-  static int cached[64];
+// A device attribute of the current device, cached per device (fallback
+// when the query fails).
+int device_attr(hipDeviceAttribute_t attr, int fallback, int (&cache)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
-    return DEFAULT_CUS;
+    return fallback;
   }
-  if (cached[dev] > 0) return cached[dev];
+  if (cache[dev] > 0) return cache[dev];
   int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+  if (hipDeviceGetAttribute(&n, attr, dev) != hipSuccess || n <= 0) {
     (void)hipGetLastError();
-    n = DEFAULT_CUS;
+    n = fallback;
   }
-  cached[dev] = n;
+  cache[dev] = n;
   return n;
+}
+
+int device_cu_count() {
+  static int cached[64];
+  return device_attr(hipDeviceAttributeMultiprocessorCount, DEFAULT_CUS, cached);
+}
+
+int device_xcd_count() {
+  static int cached[64];
+  return device_attr(hipDeviceAttributeNumberOfXccs, DEFAULT_XCDS, cached);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Plan {
   bool mfma;
+  bool wide;    // matrix cores, units of WIDE_ROWS rows sharing each tile over the waves
   int R, RB, RMAX, units;
   int W;        // workgroups launched
   int fast;     // workers given the larger share (see Partition), 0: equal shares
+  int xcds;     // workers numbered XCD by XCD (see worker_of), 0: in launch order
   int workers;  // independent workers: waves (vector-ALU kernel) or workgroups (matrix cores)
   size_t off_o, off_ml, bytes;
 };
 
 // Query-row blocks per (b, k) on the matrix cores for R rows: one block of
-// up to 64 rows; long query blocks (several row blocks anyway) take blocks of
-// at most 48 rows, whose matrix-core form runs two workgroups per CU where
-// the LDS allows (each further row block re-reads the unit's K/V rows).
-int row_blocks(int R, int H) {
-  const int nb_total = (R + 15) / 16;
-  const int max_nb = nb_total > MFMA_MAX_NB && H == 128 ? 3 : MFMA_MAX_NB;
-  return (nb_total + max_nb - 1) / max_nb;
-}
+// up to 64 rows (the per-wave form); longer query blocks take blocks of
+// WIDE_ROWS rows, whose waves share each K/V tile (each further row block
+// re-reads the unit's K/V rows).
+bool wide_rows(int R) { return (R + 15) / 16 > MFMA_MAX_NB; }
+int row_blocks(int R) { return wide_rows(R) ? (R + kvc::WIDE_ROWS - 1) / kvc::WIDE_ROWS : 1; }
 
 bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, Plan* p) {
   if (B < 1 || T < 1 || T > KVC_MAX_T || N < 1 || K < 1 || N % K || (H != 64 && H != 128) ||
@@ -84,16 +95,16 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
     return false;
   const int G = N / K;
   p->R = G * T;
+  p->wide = false;
   if (p->R <= valu_max_rows(H)) {
     p->mfma = false;
     p->RB = 1;
     p->RMAX = p->R;
   } else {
     p->mfma = true;
-    const int nb_total = (p->R + 15) / 16;
-    p->RB = row_blocks(p->R, H);
-    const int nb = (nb_total + p->RB - 1) / p->RB;
-    p->RMAX = nb * 16;
+    p->wide = wide_rows(p->R);
+    p->RB = row_blocks(p->R);
+    p->RMAX = p->wide ? kvc::WIDE_ROWS : (p->R + 15) / 16 * 16;
   }
   const int64_t units = (int64_t)B * K * p->RB;
   if (units > COUNTER_SLOTS) return false;
@@ -105,7 +116,9 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
   } else {
     const int64_t steps_ub = units * ((max_seq_len + kvc::STEP - 1) / kvc::STEP);
     const int cus = device_cu_count();
-    const int per_cu = p->mfma ? kvc::mfma_workgroups_per_cu(B, H, p->RMAX) : kvc::valu_workgroups_per_cu(B, H);
+    const int per_cu = p->wide   ? kvc::wide_workgroups_per_cu(B, H)
+                       : p->mfma ? kvc::mfma_workgroups_per_cu(B, H, p->RMAX)
+                                 : kvc::valu_workgroups_per_cu(B, H);
     const int64_t full = (int64_t)cus * per_cu;
     const int64_t unit_steps = (max_seq_len + kvc::STEP - 1) / kvc::STEP;
     int64_t want_workers = unit_steps <= SHORT_UNIT_STEPS
@@ -119,6 +132,12 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
     // older of a CU's pair
     p->fast = per_cu == 2 && p->W == full ? cus : 0;
   }
+  // Several row blocks per (b, k) read the same K/V rows: number the
+  // workers XCD by XCD so that consecutive row blocks mostly share an L2
+  // (the weighted shares assume launch order, so they are dropped).
+  const int xcds = device_xcd_count();
+  p->xcds = p->mfma && p->RB > 1 && xcds > 1 && p->W % xcds == 0 ? xcds : 0;
+  if (p->xcds) p->fast = 0;
   p->workers = p->W * per_wg;
   const size_t slots = (size_t)p->workers + (size_t)p->units;
   p->off_ml = (size_t)COUNTER_SLOTS * sizeof(int32_t);
@@ -208,7 +227,7 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   if (!aligned16(q) || !aligned16(out)) return KVC_ERR_INVALID;
   const bool fused = k_new != nullptr || v_new != nullptr;
   if (fused && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return KVC_ERR_INVALID;
-  if ((int64_t)B * K * (N / K * T <= valu_max_rows(H) ? 1 : row_blocks(N / K * T, H)) > COUNTER_SLOTS)
+  if ((int64_t)B * K * (N / K * T <= valu_max_rows(H) ? 1 : row_blocks(N / K * T)) > COUNTER_SLOTS)
     return KVC_ERR_UNSUPPORTED;
   // a window bounds the keys any call streams per unit: at most
   // window + T - 1 positions, starting anywhere inside a 128-token step
@@ -248,6 +267,7 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   a.out_dtype = out_dtype;
   a.W = p.workers;
   a.fast_workers = p.fast;
+  a.xcds = p.xcds;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.window = window;
   a.tree = tree;
@@ -269,8 +289,9 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
     fill_copy_args(&ca, c, capacity, shift, k_new, v_new, B, T, K, H, seq_lens);
     if (kvc::launch_append(ca, paged, s) != hipSuccess) return KVC_ERR_HIP;
   }
-  const hipError_t e = p.mfma ? kvc::launch_attn_mfma(a, bf, H, paged, s)
-                              : kvc::launch_attn_valu(a, bf, H, paged, s);
+  const hipError_t e = p.wide   ? kvc::launch_attn_wide(a, bf, H, paged, s)
+                       : p.mfma ? kvc::launch_attn_mfma(a, bf, H, paged, s)
+                                : kvc::launch_attn_valu(a, bf, H, paged, s);
   return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 

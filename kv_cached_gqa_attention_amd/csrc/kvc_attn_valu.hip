@@ -70,7 +70,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a);
-  const Partition part = make_partition(a, s_pre, blockIdx.x);
+  const int worker = worker_of(a, blockIdx.x);
+  const Partition part = make_partition(a, s_pre, worker);
   append_owned<H, THREADS, PAGED>(a, s_pre, part);
   if (part.lo >= part.hi) return;  // the whole workgroup: no barrier is skipped
 
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    finish_segment<H, WAVES>(a, g, blockIdx.x, s_m, s_l, s_o, s_w, segbad, shared);
+    finish_segment<H, WAVES>(a, g, worker, s_m, s_l, s_o, s_w, segbad, shared);
 
     if (cs.x + 1 >= part.hi) break;
     cs.advance(a, s_pre, part);

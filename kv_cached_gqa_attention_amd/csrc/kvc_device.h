@@ -65,6 +65,7 @@ struct AttnArgs {
   int32_t out_dtype;  // 0 f16, 1 bf16, 2 f32
   int32_t W;          // workers sharing the tiles (waves or workgroups, per kernel)
   int32_t fast_workers;  // the first fast_workers get the larger share (0: equal shares)
+  int32_t xcds;       // > 0: workers numbered XCD by XCD (worker_of); 0: worker = workgroup
   float scale_log2;   // scale * log2(e)
   float* part_o;      // [W + units, RMAX, H], slot = worker + unit
   float* part_ml;     // [W + units, RMAX, 2]
@@ -362,6 +363,17 @@ struct Partition {
     return (int)(w < w_eff - 1 ? w : w_eff - 1);
   }
 };
+
+// The worker a workgroup plays. Workgroups are dealt to the XCDs round
+// robin (workgroup i runs on XCD i mod xcds), each XCD with its own L2; with
+// xcds > 0 (and W a multiple of it) the workers of one XCD are consecutive,
+// so the consecutive row blocks of one (b, k), which read the same K and V
+// rows, mostly share an L2.
+__device__ __forceinline__ int worker_of(const AttnArgs& a, int wg) {
+  if (a.xcds <= 0) return wg;
+  const int per = a.W / a.xcds;
+  return (wg % a.xcds) * per + wg / a.xcds;
+}
 
 __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int32_t* s_pre,
                                                     int w) {

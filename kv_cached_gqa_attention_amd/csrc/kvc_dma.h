@@ -145,7 +145,9 @@ struct StepCursor {
 // chunk positions). One instruction covers RPI = 64 / (ROWB / 16)
 // consecutive rows; lane L reads row i * RPI + L / CPR of instruction i,
 // whose in-tile byte offset lvoff[i] (row * stride_tok + 16 * chunk) the
-// kernel computes once (tile_lane_offsets).
+// kernel computes once (tile_lane_offsets). copy_tile_part issues only the
+// NIW instructions i0 .. i0 + NIW - 1 (a wave's share when the waves of a
+// workgroup copy one tile together), lvoff holding their offsets.
 //
 // Tiles wholly inside the visible rows take a uniform base per block: with a
 // block table, a block of at least TILE rows holds the whole tile (one
@@ -156,28 +158,27 @@ struct StepCursor {
 // take per-lane entries (vector loads, which the compiler waits for,
 // together with every copy issued before them). An entry outside the pool
 // reads block 0 and sets `bad`.
-template <int H, typename Swz>
-__device__ __forceinline__ void tile_lane_offsets(const AttnArgs& a, int lane, Swz swz,
-                                                  uint32_t (&lvoff)[TILE * H * 2 / 1024]) {
+template <int H, int NIW = TILE * H * 2 / 1024, typename Swz>
+__device__ __forceinline__ void tile_lane_offsets(const AttnArgs& a, int lane, Swz swz, uint32_t (&lvoff)[NIW],
+                                                  int i0 = 0) {
   constexpr int CPR = H * 2 / 16;
   constexpr int RPI = 64 / CPR;
   const int rl = lane / CPR;
   const int p = lane % CPR;
 #pragma unroll
-  for (int i = 0; i < TILE / RPI; ++i) {
-    const int r = i * RPI + rl;
+  for (int i = 0; i < NIW; ++i) {
+    const int r = (i0 + i) * RPI + rl;
     lvoff[i] = (uint32_t)r * (uint32_t)a.stride_tok + (uint32_t)(p ^ swz(r)) * 16u;
   }
 }
 
-template <int H, bool PAGED, bool MASKED, typename Swz>
-__device__ __forceinline__ void copy_tile(const AttnArgs& a, const Segment& g, const char* base,
-                                          int first, uint32_t lds, int lane, Swz swz,
-                                          const uint32_t (&lvoff)[TILE * H * 2 / 1024], bool& bad) {
+template <int H, bool PAGED, bool MASKED, int NIW, typename Swz>
+__device__ __forceinline__ void copy_tile_part(const AttnArgs& a, const Segment& g, const char* base,
+                                               int first, uint32_t lds, int lane, Swz swz,
+                                               const uint32_t (&lvoff)[NIW], int i0, bool& bad) {
   constexpr int ROWB = H * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int RPI = 64 / CPR;
-  constexpr int NI = TILE / RPI;
   const int last = g.seq_len - 1;
   const int vis0 = MASKED ? first_visible(a, g.seq_len) : 0;
   const int64_t trow = PAGED ? (int64_t)g.b * a.max_blocks : 0;
@@ -195,26 +196,27 @@ __device__ __forceinline__ void copy_tile(const AttnArgs& a, const Segment& g, c
       sb = base + (int64_t)first * a.stride_tok;
     }
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(sb, lvoff[i], lds + i * 1024);
+    for (int i = 0; i < NIW; ++i) dma16(sb, lvoff[i], lds + (i0 + i) * 1024);
     return;
   }
   if (PAGED && first >= vis0 && first + TILE - 1 <= last && (1 << a.block_shift) >= RPI) {
     // blocks of RPI..TILE-1 rows: a new entry where a block starts (tiles
-    // start on a block boundary here)
+    // start on a block boundary here), and for the first instruction
     const char* sb = base;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if (((i * RPI) & bmask) == 0) {
-        int blk = load_uniform(a.table, trow + ((first + i * RPI) >> a.block_shift));
+    for (int i = 0; i < NIW; ++i) {
+      const int r0 = (i0 + i) * RPI;  // the instruction's first row in the tile
+      if (i == 0 || (r0 & bmask) == 0) {
+        int blk = load_uniform(a.table, trow + ((first + r0) >> a.block_shift));
         if ((unsigned)blk >= (unsigned)a.num_blocks) {
           bad = true;
           blk = 0;
         }
         // lvoff[i] counts rows from the tile's start
-        sb = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(base) + (int64_t)blk * a.stride_seq -
-                                           (int64_t)(i * RPI) * a.stride_tok);
+        sb = reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(base) + (int64_t)blk * a.stride_seq +
+                                           (int64_t)((r0 & bmask) - r0) * a.stride_tok);
       }
-      dma16(sb, lvoff[i], lds + i * 1024);
+      dma16(sb, lvoff[i], lds + (i0 + i) * 1024);
     }
     return;
   }
@@ -223,10 +225,10 @@ __device__ __forceinline__ void copy_tile(const AttnArgs& a, const Segment& g, c
   const int p = lane % CPR;
   const uint32_t stok = (uint32_t)a.stride_tok;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = i * RPI + rl;
+  for (int i = 0; i < NIW; ++i) {
+    const int r = (i0 + i) * RPI + rl;
     const uint32_t jb = (uint32_t)(p ^ swz(r)) * 16u;
-    const int t0 = first + i * RPI;
+    const int t0 = first + (i0 + i) * RPI;
     int tb = min(t0, last);
     if constexpr (MASKED) tb = max(tb, vis0);
     int tok = min(t0 + rl, last);
@@ -239,7 +241,7 @@ __device__ __forceinline__ void copy_tile(const AttnArgs& a, const Segment& g, c
           blk = 0;
         }
         dma16_addr(base + (int64_t)blk * a.stride_seq + (int64_t)(tok & bmask) * a.stride_tok + jb,
-                   lds + i * 1024);
+                   lds + (i0 + i) * 1024);
       } else {
         // tb and every clamped row of this instruction share one block
         int blk = load_uniform(a.table, trow + (tb >> a.block_shift));
@@ -248,12 +250,20 @@ __device__ __forceinline__ void copy_tile(const AttnArgs& a, const Segment& g, c
           blk = 0;
         }
         const char* sb = base + (int64_t)blk * a.stride_seq + (int64_t)(tb & bmask) * a.stride_tok;
-        dma16(sb, (uint32_t)(tok - tb) * stok + jb, lds + i * 1024);
+        dma16(sb, (uint32_t)(tok - tb) * stok + jb, lds + (i0 + i) * 1024);
       }
     } else {
-      dma16(base + (int64_t)tb * a.stride_tok, (uint32_t)(tok - tb) * stok + jb, lds + i * 1024);
+      dma16(base + (int64_t)tb * a.stride_tok, (uint32_t)(tok - tb) * stok + jb, lds + (i0 + i) * 1024);
     }
   }
+}
+
+// The whole tile (every instruction), as one wave copies it.
+template <int H, bool PAGED, bool MASKED, typename Swz>
+__device__ __forceinline__ void copy_tile(const AttnArgs& a, const Segment& g, const char* base,
+                                          int first, uint32_t lds, int lane, Swz swz,
+                                          const uint32_t (&lvoff)[TILE * H * 2 / 1024], bool& bad) {
+  copy_tile_part<H, PAGED, MASKED, TILE * H * 2 / 1024>(a, g, base, first, lds, lane, swz, lvoff, 0, bad);
 }
 
 }  // namespace kvc

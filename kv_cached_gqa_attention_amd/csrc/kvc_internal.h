@@ -31,5 +31,9 @@ int valu_workgroups_per_cu(int B, int H);
 // Workgroups of the matrix-core kernel per CU for B sequences and RMAX rows.
 int mfma_workgroups_per_cu(int B, int H, int RMAX);
 hipError_t launch_attn_mfma(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream);
+// Long query blocks: units of WIDE_ROWS rows whose four waves share each K/V tile.
+constexpr int WIDE_ROWS = 128;
+int wide_workgroups_per_cu(int B, int H);
+hipError_t launch_attn_wide(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream);
 
 }  // namespace kvc

@@ -320,6 +320,83 @@ def test_prefill_chunk_fused_and_any_workgroup_count(gpu_device, case):
         compare_units(run, all_units(run.inp))
 
 
+# Long query blocks run on units of 128 rows whose four waves share every K/V
+# tile (each wave copies a quarter of it); these cases take that path through
+# its masks, block sizes, grids and launch forms.
+WIDE = [PREFILL[0], PREFILL[1], (2, 20, 16, 4, 64, HF, [500, 3])]  # G*T = 256, 1400, 80
+
+
+@pytest.mark.parametrize("W", [1, 40, 129, 1000])
+@pytest.mark.parametrize("case", WIDE, ids=_ids(WIDE))
+def test_prefill_chunk_with_window(gpu_device, case, W):
+    B, T, N, K, H, dtype, prior = case
+    run = run_case(B, T, N, K, H, dtype, prior, layout="paged", seed=320 + W, window=W)
+    compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("T,N,K,H", [(32, 16, 2, 128), (20, 32, 4, 64)])
+def test_long_blocks_with_a_draft_tree(gpu_device, T, N, K, H, fused):
+    """Tree masks on units of 128 rows (G*T = 256: two row blocks; 160),
+    with and without a window."""
+    B = 3
+    rng = np.random.default_rng(330 + T)
+    words = _random_tree_words(rng, B, T)
+    for window in (0, 45):
+        run = run_case(B, T, N, K, H, BF, [90, 0, 700], seed=331 + T, tree=words, window=window,
+                       fused=fused)
+        compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("bs", [1, 2, 8, 32, 256])
+@pytest.mark.parametrize("H", [64, 128])
+def test_prefill_chunk_any_block_size(gpu_device, bs, H):
+    """Blocks smaller than one copy instruction's rows (per-lane entries),
+    blocks holding whole instructions, and blocks of one or more tiles; each
+    wave's quarter of a tile looks up its own blocks."""
+    run = run_case(2, 40, 16, 4, H, BF, [77, 300], layout="paged", block_size=bs, seed=340 + bs)
+    compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("nwg", [8, 16, 64, 40, 3, 1000])
+def test_prefill_chunk_workgroup_counts(gpu_device, nwg):
+    """Grids whose size is a multiple of the XCD count number their workers
+    XCD by XCD (several row blocks per (b, k)); others in launch order."""
+    run = run_case(3, 64, 32, 8, 128, BF, [1500, 0, 333], seed=350, num_workgroups=nwg)
+    compare_units(run, all_units(run.inp))
+
+
+def test_prefill_chunk_out_of_range_block_entry(gpu_device):
+    """An entry outside the pool, met by one wave's quarter of a tile, makes
+    that sequence's rows NaN (every wave's rows) and no other sequence's."""
+    dev = gpu_device
+    B, T, N, K, H = 3, 40, 16, 4, 128
+    inp = draw_inputs(B, T, N, K, H, BF, np.array([100, 100, 100]), seed=360, device=dev)
+    table, nb = make_block_table(361, inp.seq_lens, 8)
+    pk, pv = layout_paged(inp, table, nb, 8)
+    seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(dev)
+    cache = kvc.Cache(pk, pv, torch.from_numpy(table).to(dev))
+    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+    bad = table.copy()
+    bad[1, 5] = nb + 1000  # rows 40..47: the second wave's quarter of tile 1
+    cache_bad = kvc.Cache(pk, pv, torch.from_numpy(bad).to(dev))
+    out = kvc.verify(inp.q, cache_bad, seq_lens, int(inp.seq_lens.max()), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all()
+    assert torch.isfinite(out[0]).all() and torch.isfinite(out[2]).all()
+
+
+def test_prefill_chunk_large_batch(gpu_device):
+    """A batch whose prefix table leaves room for one workgroup per CU (a
+    longer ring of halves), sampled units against the oracle."""
+    B = 1500
+    prior = np.random.default_rng(370).integers(0, 200, size=B)
+    run = run_case(B, 17, 8, 2, 128, BF, prior, layout="paged", seed=371)
+    rng = np.random.default_rng(372)
+    units = [(int(b), int(k)) for b, k in zip(rng.integers(0, B, 40), rng.integers(0, 2, 40))]
+    compare_units(run, units + [(0, 0), (B - 1, 1)])
+
+
 # ----------------------------------------------------------------- fused append + attend
 
 FUSED = [SMALL[0], SMALL[3], SMALL[5], SMALL[7], SMALL[9], SMALL[11], SMALL[12], SMALL[13]]
