@@ -343,7 +343,10 @@ def main():
     # balance against HBM (a chunk of prefill), else HBM
     step_flops = attn_flops(w, seq_lens)
     mfma_bound = step_flops / step_bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    kernel = "attn_mfma_kernel" if w.G * w.T > (8 if w.H == 64 else 4) else "attn_valu_kernel"
+    # the kernel that serves the workload's query blocks (as the library plans it)
+    rows = w.G * w.T
+    kernel = ("attn_wide_kernel" if rows > 64
+              else "attn_mfma_kernel" if rows > (8 if w.H == 64 else 4) else "attn_valu_kernel")
     traffic = profiled_traffic(kernel, w.name)
 
     value = step_bytes * layers / (ms_per_step * 1e-3) / 1e9
