@@ -386,6 +386,43 @@ def test_prefill_chunk_out_of_range_block_entry(gpu_device):
     assert torch.isfinite(out[0]).all() and torch.isfinite(out[2]).all()
 
 
+def test_prefill_chunk_invalid_lengths_give_nan_rows_only(gpu_device):
+    """Long query blocks: sequences whose length is below T or above the
+    capacity give NaN rows (outputs and LSE); the others match the oracle."""
+    dev = gpu_device
+    B, T, N, K, H = 4, 40, 8, 2, 128
+    inp = draw_inputs(B, T, N, K, H, BF, np.array([30, 40, 50, 60]), seed=365, device=dev)
+    ck, cv = layout_contiguous(inp, capacity=128)
+    cache = kvc.Cache(ck, cv)
+    lens = inp.seq_lens.astype(np.int32).copy()
+    lens[1] = 39          # < T
+    lens[3] = 129         # > capacity
+    seq_lens = torch.from_numpy(lens).to(dev)
+    kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+    out, lse = kvc.verify(inp.q, cache, seq_lens, 128, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all() and torch.isnan(out[3]).all()
+    assert torch.isnan(lse[1]).all() and torch.isnan(lse[3]).all()
+    G = N // K
+    for b in (0, 2):
+        for k in range(K):
+            o_ref, l_ref = oracle_unit(inp, b, k, 1 / math.sqrt(H))
+            got = out[b, :, k * G : (k + 1) * G].double().cpu().numpy()
+            assert np.abs(got - o_ref).max() <= 2e-3
+            assert np.abs(lse[b, :, k * G : (k + 1) * G].double().cpu().numpy() - l_ref).max() <= 2e-3
+
+
+def test_long_blocks_one_row_block_full_grid(gpu_device):
+    """80 rows per (b, k) (one row block) over enough units for a full
+    automatic grid: the two workgroups of a CU take weighted shares."""
+    B = 64
+    prior = np.random.default_rng(380).integers(300, 700, size=B)
+    run = run_case(B, 20, 16, 4, 128, BF, prior, seed=381)
+    rng = np.random.default_rng(382)
+    units = [(int(b), int(k)) for b, k in zip(rng.integers(0, B, 40), rng.integers(0, 4, 40))]
+    compare_units(run, units + [(0, 0), (B - 1, 3)])
+
+
 def test_prefill_chunk_large_batch(gpu_device):
     """A batch whose prefix table leaves room for one workgroup per CU (a
     longer ring of halves), sampled units against the oracle."""
