@@ -10,9 +10,9 @@
 // quarter of its copy instructions), and a barrier per tile makes all
 // quarters visible and frees the slots of the tile before. One fetch of a
 // K/V row thus serves 128 query rows, where the per-wave form (each wave its
-// own tile for all of the unit's rows) serves at most 48; with the fetches
-// of long blocks re-read once per row block, that is what bounds the
-// per-wave form on prefill-sized chunks.
+// own tile for all of the unit's rows) serves at most 64; long blocks re-read
+// the K/V rows once per row block, and with fewer rows per block those
+// re-reads bound the per-wave form on prefill-sized chunks.
 //
 // Per tile and wave the arithmetic is that of the per-wave form
 // (v_mfma_f32_16x16x32_{bf16,f16}, transposed score block, p split into a
