@@ -394,8 +394,16 @@ def main():
             "bytes_per_launch": step_bytes,
         },
     }
+    tflops = step_flops / (attn_ms * 1e-3) / 1e12
+    if kernel != "attn_valu_kernel" and not mfma_bound:
+        # a matrix-core kernel bound by HBM: its matrix-core use beside the
+        # HBM figure (algorithmic flops over the dense bf16/fp16 peak)
+        result["roofline"].update({
+            "flops_per_launch": step_flops,
+            "mfma_tflops": round(tflops, 2),
+            "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+        })
     if mfma_bound:
-        tflops = step_flops / (attn_ms * 1e-3) / 1e12
         result["roofline"].update({
             "bound": "mfma",
             "achieved": round(tflops, 2),
