@@ -72,6 +72,26 @@ def test_workspace_bytes(lib):
     assert 0 < a < b
 
 
+def test_workspace_layout_follows_the_row_block_rule(lib):
+    """The workspace is the counter array, then per slot (worker or unit) the
+    row statistics and the fp32 rows of a partial. Row blocks hold all G*T
+    rows up to 64 (vector path up to 4 at H = 128) and 128 rows beyond, so
+    the size pins the rule the header states."""
+    counters = 1 << 18
+
+    def expect(units, workers, rmax, H):
+        up = lambda x: (x + 255) // 256 * 256
+        slots = workers + units
+        return counters * 4 + up(slots * rmax * 2 * 4) + up(slots * rmax * H * 4)
+
+    W = 100  # an explicit grid: the automatic one depends on the device
+    B, K, H = 8, 8, 128
+    for T, N, rmax, rb in [(1, 32, 4, 1), (5, 64, 48, 1), (16, 32, 64, 1), (17, 32, 128, 1),
+                           (32, 32, 128, 1), (33, 32, 128, 2), (512, 32, 128, 16)]:
+        got = lib.kvc_workspace_bytes(B, T, N, K, H, 4097, W)
+        assert got == expect(B * K * rb, W, rmax, H), (T, N)
+
+
 def _cache(**kw):
     c = _lib.KvcCache()
     c.k = FAKE
