@@ -117,18 +117,33 @@ def workspace_bytes(B, T, N, K, H, max_seq_len, num_workgroups=0) -> int:
 
 
 _ws_cache: dict = {}
+# Buffers replaced by a larger one stay referenced until the process ends: a
+# call still queued on the GPU (or a graph captured with an explicit buffer
+# taken from here) may point at them, so they are never handed back to the
+# allocator.
+_ws_retired: list = []
 
 
-def workspace(device, nbytes: int) -> torch.Tensor:
-    """A zero-filled workspace of at least ``nbytes``, reused per device.
+def workspace(device, nbytes: int, stream=None) -> torch.Tensor:
+    """A zero-filled workspace of at least ``nbytes``, reused per (device,
+    stream).
 
-    The library leaves it zero-filled after every call, so one buffer serves
-    every call on one stream.
+    The library leaves the counter region zero after every call, so one
+    buffer serves every call on one stream; calls on different streams may
+    overlap in time and get different buffers. During stream capture there
+    is no implicit workspace: pass one explicitly, so the captured graph
+    owns memory that outlives it.
     """
     device = torch.device(device)
-    key = (device.type, device.index)
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("kvc: pass an explicit workspace (ws=...) when capturing a graph")
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    key = (device.type, device.index, stream.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
+        if buf is not None:
+            _ws_retired.append(buf)
         buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf

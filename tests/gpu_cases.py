@@ -110,11 +110,12 @@ def to_device(inp, device):
     return out
 
 
-def oracle_unit(inp, b, k, scale, window=0, tree=None):
+def oracle_unit(inp, b, k, scale, window=0, tree=None, kv=None):
     """Oracle output [T, G, H] and lse [T, G] of sequence b, key-value head k
-    (optionally with a window and the sequence's tree words)."""
+    (optionally with a window and the sequence's tree words; ``kv``: the
+    sequence's logical K and V when already gathered)."""
     G = inp.N // inp.K
-    kb, vb = logical_kv(inp, b)
+    kb, vb = logical_kv(inp, b) if kv is None else kv
     kk = kb[:, k : k + 1, :].double().cpu().numpy()
     vv = vb[:, k : k + 1, :].double().cpu().numpy()
     q = inp.q[b : b + 1, :, k * G : (k + 1) * G, :].double().cpu().numpy()
@@ -128,8 +129,11 @@ def compare_units(run, units, out_tol=TOL, lse_tol=TOL):
     inp = run.inp
     G = inp.N // inp.K
     worst_o = worst_l = 0.0
-    for b, k in units:
-        o_ref, l_ref = oracle_unit(inp, b, k, run.scale, run.window, run.tree)
+    kv_b, kv = None, None
+    for b, k in sorted(units):
+        if b != kv_b:  # gather each sequence's logical rows once
+            kv_b, kv = b, logical_kv(inp, b)
+        o_ref, l_ref = oracle_unit(inp, b, k, run.scale, run.window, run.tree, kv=kv)
         o = run.out[b, :, k * G : (k + 1) * G, :].double().cpu().numpy()
         l = run.lse[b, :, k * G : (k + 1) * G].double().cpu().numpy()
         assert np.all(np.isfinite(o)), f"non-finite output in unit {(b, k)}"
