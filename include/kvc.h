@@ -258,6 +258,35 @@ kvc_status kvc_attn(const kvc_cache *cache, const kvc_attn_options *opts, const 
                     const int32_t *seq_lens, int max_seq_len, float scale, int num_workgroups,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the per-device scratch array kvc_attn_noalloc runs in. */
+#define KVC_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Exactly
+ * kvc_attn (same arguments, options, kernels and results) without the
+ * workspace arguments: the counters and partials live in a static device
+ * array of KVC_NOALLOC_SCRATCH_BYTES bytes inside the library, one per
+ * device, held from this entry point's first call on that device until the
+ * process ends. That first call on a device takes the array's address and
+ * clears its counter region on `stream`; every completed call leaves the
+ * counters zero again. Nothing is allocated or freed, ever; the caller still
+ * passes q, out, lse and the cache.
+ * All calls on one device share that device's array: calls that overlap in
+ * time on one device (different streams, threads) race and give undefined
+ * results; serialise them (one stream, or events).
+ * Errors: as kvc_attn, plus KVC_ERR_WORKSPACE (before anything is launched)
+ * when the call needs more than KVC_NOALLOC_SCRATCH_BYTES, i.e. when
+ * kvc_workspace_bytes(B, T, N, K, H, max_seq_len, num_workgroups) exceeds
+ * it (e.g. chunks of prefill of 512 tokens for 8 sequences of 8 key-value
+ * heads; a smaller num_workgroups lowers the need); KVC_ERR_HIP when the
+ * array's address cannot be taken.
+ */
+kvc_status kvc_attn_noalloc(const kvc_cache *cache, const kvc_attn_options *opts, const void *q,
+                            void *out, int out_dtype, float *lse, int B, int T, int N, int K,
+                            int H, const int32_t *seq_lens, int max_seq_len, float scale,
+                            int num_workgroups, void *stream);
+
 /*
  * Host query: workspace bytes needed by kvc_attn_decode (T = 1) or
  * kvc_attn_verify with the same B, T, N, K, H, max_seq_len and

@@ -12,6 +12,7 @@ from .api import (
     append,
     append_attend,
     attend,
+    attend_noalloc,
     decode,
     gather,
     status_string,
@@ -26,6 +27,7 @@ __all__ = [
     "append",
     "append_attend",
     "attend",
+    "attend_noalloc",
     "decode",
     "gather",
     "status_string",

@@ -23,6 +23,7 @@ KVC_BF16 = 1
 KVC_F32 = 2
 
 KVC_MAX_T = 2048  # new tokens per sequence in one attention call (include/kvc.h)
+KVC_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static scratch of kvc_attn_noalloc (include/kvc.h)
 
 # Every symbol the header declares, in declaration order.
 EXPORTS = (
@@ -31,6 +32,7 @@ EXPORTS = (
     "kvc_attn_verify",
     "kvc_append_attend",
     "kvc_attn",
+    "kvc_attn_noalloc",
     "kvc_workspace_bytes",
     "kvc_status_string",
     "kvc_gather",
@@ -101,6 +103,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvc_attn.argtypes = [cache_p, opts_p, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
                              vp, c_int, ctypes.c_float, c_int, vp, c_size_t, vp]
     lib.kvc_attn.restype = c_int
+    lib.kvc_attn_noalloc.argtypes = [cache_p, opts_p, vp, vp, c_int, vp, c_int, c_int, c_int, c_int,
+                                     c_int, vp, c_int, ctypes.c_float, c_int, vp]
+    lib.kvc_attn_noalloc.restype = c_int
     lib.kvc_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int]
     lib.kvc_workspace_bytes.restype = c_size_t
     lib.kvc_status_string.argtypes = [c_int]

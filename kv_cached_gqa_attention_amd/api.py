@@ -289,6 +289,59 @@ def attend(q, cache: Cache, seq_lens, max_seq_len, window=0, tree_mask=None, k_n
                  ws, T, opts=opts)
 
 
+def attend_noalloc(q, cache: Cache, seq_lens, max_seq_len, out, lse=None, window=0, tree_mask=None,
+                   k_new=None, v_new=None, scale=None, num_workgroups=0):
+    """``attend`` without any allocation: ``kvc_attn_noalloc``.
+
+    The caller passes ``out`` (q's shape; fp32, fp16 or bf16) and optionally
+    ``lse`` (fp32, q's shape without the head dim); the counters and partials
+    live in the library's per-device static scratch, so calls that overlap in
+    time on one device must not be issued (they share it). Nothing here
+    allocates device memory.
+    """
+    if q.dim() not in (3, 4):
+        raise ValueError("attend_noalloc takes q [B, N, H] or [B, T, N, H]")
+    _gpu(q, "q")
+    _gpu(seq_lens, "seq_lens")
+    _gpu(out, "out")
+    if not q.is_contiguous() or q.dtype != cache.k.dtype:
+        raise ValueError("q must be contiguous with the cache dtype")
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if out.shape != q.shape or not out.is_contiguous() or out.dtype not in _DT:
+        raise ValueError("out must be contiguous with q's shape (fp32, fp16 or bf16)")
+    if lse is not None:
+        _gpu(lse, "lse")
+        if lse.shape != q.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be contiguous fp32 with q's shape minus the head dim")
+    T = 1 if q.dim() == 3 else q.shape[1]
+    B, N, H = q.shape[0], q.shape[-2], q.shape[-1]
+    opts = _lib.KvcAttnOptions()
+    opts.window = int(window)
+    if tree_mask is not None:
+        _gpu(tree_mask, "tree_mask")
+        if tree_mask.dtype != torch.int32 or tuple(tree_mask.shape) != (B, T) or not tree_mask.is_contiguous():
+            raise ValueError("tree_mask must be contiguous int32 [B, T]")
+        opts.tree_mask = _ptr(tree_mask)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _check_new_rows(cache, k_new, v_new, seq_lens)
+        if k_new.shape[0] != B or k_new.shape[1] != T:
+            raise ValueError("k_new must be [B, T, K, H] for q's B and T")
+        opts.k_new = _ptr(k_new)
+        opts.v_new = _ptr(v_new)
+    if scale is None:
+        scale = 1.0 / math.sqrt(H)
+    desc = cache.descriptor()
+    st = _lib.load().kvc_attn_noalloc(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(out),
+                                      _DT[out.dtype], _ptr(lse), B, T, N, cache.num_kv_heads, H,
+                                      _ptr(seq_lens), int(max_seq_len), float(scale),
+                                      int(num_workgroups), _stream(q.device))
+    _check(st, "kvc_attn_noalloc")
+    return out
+
+
 def gather(cache: Cache, seq_lens, max_seq_len):
     """Paged cache -> contiguous (k, v) [B, K, max_seq_len, H]; rows past seq_lens[b] are zero."""
     if not cache.paged:

@@ -10,8 +10,17 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvc.h"
 #include "kvc_internal.h"
+
+// Scratch of kvc_attn_noalloc: the same layout as a caller's workspace
+// (counters, then partials), one copy per device, held until the process
+// ends. Host code never uses this name as an address (on the host it is a
+// stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device (noalloc_scratch below).
+static __device__ __align__(256) char scratch[KVC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -204,10 +213,38 @@ void fill_copy_args(CopyArgs* a, const kvc_cache* c, int capacity, int shift, co
 
 // Attention, optionally preceded by the append of k_new / v_new (fused: one
 // launch when every (b, k) is one unit, else an append launch first).
+// The device address of this device's `scratch` array, taken once per
+// device (with that device current); at that first use the counter region is
+// cleared on `stream` (every completed call leaves it zero again).
+struct DeviceScratch {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+DeviceScratch g_scratch[64];
+
+hipError_t noalloc_scratch(void** out, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  DeviceScratch& d = g_scratch[dev];
+  std::call_once(d.once, [&] {
+    void* p = nullptr;
+    d.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (d.err == hipSuccess) d.err = kvc::launch_zero(p, (size_t)COUNTER_SLOTS * sizeof(int32_t), stream);
+    if (d.err == hipSuccess) d.ptr = p;
+  });
+  *out = d.ptr;
+  return d.err;
+}
+
+// ws == nullptr with static_ws: the call runs in this device's `scratch`
+// array (kvc_attn_noalloc), after the same checks.
 kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dtype, float* lse,
                        int B, int T, int N, int K, int H, const int32_t* seq_lens, int max_seq_len,
                        float scale, int num_wg, void* ws, size_t ws_bytes, void* stream,
-                       const kvc_attn_options* opts = nullptr) {
+                       const kvc_attn_options* opts = nullptr, bool static_ws = false) {
   const void* k_new = opts ? opts->k_new : nullptr;
   const void* v_new = opts ? opts->v_new : nullptr;
   const int window = opts ? opts->window : 0;
@@ -238,6 +275,11 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   }
   Plan p;
   if (!make_plan(B, T, N, K, H, span, num_wg, &p)) return KVC_ERR_INVALID;
+  if (static_ws) {
+    if (p.bytes > (size_t)KVC_NOALLOC_SCRATCH_BYTES) return KVC_ERR_WORKSPACE;
+    if (noalloc_scratch(&ws, static_cast<hipStream_t>(stream)) != hipSuccess) return KVC_ERR_HIP;
+    ws_bytes = KVC_NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws || ws_bytes < p.bytes || !aligned16(ws)) return KVC_ERR_WORKSPACE;
 
   AttnArgs a;
@@ -351,6 +393,15 @@ kvc_status kvc_attn(const kvc_cache* cache, const kvc_attn_options* opts, const 
   if (opts && B > 0 && opts->tree_mask && ((uintptr_t)opts->tree_mask & 3u)) return KVC_ERR_INVALID;
   return attn_common(cache, q, out, out_dtype, lse, B, T, N, K, H, seq_lens, max_seq_len, scale,
                      num_workgroups, workspace, workspace_bytes, stream, opts);
+}
+
+kvc_status kvc_attn_noalloc(const kvc_cache* cache, const kvc_attn_options* opts, const void* q,
+                            void* out, int out_dtype, float* lse, int B, int T, int N, int K, int H,
+                            const int32_t* seq_lens, int max_seq_len, float scale,
+                            int num_workgroups, void* stream) {
+  if (opts && B > 0 && opts->tree_mask && ((uintptr_t)opts->tree_mask & 3u)) return KVC_ERR_INVALID;
+  return attn_common(cache, q, out, out_dtype, lse, B, T, N, K, H, seq_lens, max_seq_len, scale,
+                     num_workgroups, nullptr, 0, stream, opts, true);
 }
 
 size_t kvc_workspace_bytes(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups) {

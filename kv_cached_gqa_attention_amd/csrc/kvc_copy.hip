@@ -69,6 +69,13 @@ __global__ __launch_bounds__(256) void gather_kernel(CopyArgs a) {
   }
 }
 
+// Zero `n16` 16-byte words at p (vector stores).
+__global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 static unsigned grid_for(int64_t work) {
   int64_t blocks = (work + 255) / 256;
   if (blocks > 65536) blocks = 65536;
@@ -81,6 +88,12 @@ hipError_t launch_append(const CopyArgs& a, bool paged, hipStream_t stream) {
     hipLaunchKernelGGL(append_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(append_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n16)), dim3(256), 0, stream, static_cast<uint4*>(p), n16);
   return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@ struct CopyArgs {
 
 hipError_t launch_append(const CopyArgs& a, bool paged, hipStream_t stream);
 hipError_t launch_gather(const CopyArgs& a, hipStream_t stream);
+// Zero `bytes` (a multiple of 16) at the 16-byte aligned device address p.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream);
 // Workgroups of the vector-ALU kernel that fit one CU's LDS for B sequences.
 int valu_workgroups_per_cu(int B, int H);

@@ -228,3 +228,38 @@ def test_attn_options_layout_and_errors(lib):
     assert at(B=0) == E.KVC_OK
     assert at(B=0, opts=False) == E.KVC_OK
     assert at(B=0, window=7, tree=FAKE) == E.KVC_OK
+
+
+def test_noalloc_host_errors(lib):
+    """kvc_attn_noalloc checks what kvc_attn checks, and rejects a call whose
+    scratch need exceeds its static array before touching the device."""
+    E = _lib
+    import re
+
+    hdr = open(HEADER).read()
+    m = re.search(r"#define KVC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.KVC_NOALLOC_SCRATCH_BYTES
+    c = _cache(capacity=8192, stride_seq=8 * 8192 * 128, stride_head=8192 * 128)
+
+    def na(B=8, T=5, N=64, L=4096, window=0, tree=None, nwg=0, q=FAKE):
+        o = _lib.KvcAttnOptions()
+        o.window = window
+        o.tree_mask = tree
+        return lib.kvc_attn_noalloc(ctypes.byref(c), ctypes.byref(o), q, FAKE, E.KVC_F32, None, B,
+                                    T, N, 8, 128, FAKE, L, 0.1, nwg, None)
+
+    assert na(T=0) == E.KVC_ERR_INVALID
+    assert na(N=60) == E.KVC_ERR_INVALID
+    assert na(window=-1) == E.KVC_ERR_INVALID
+    assert na(tree=FAKE + 2) == E.KVC_ERR_INVALID
+    assert na(q=None) == E.KVC_ERR_INVALID
+    assert na(L=8193) == E.KVC_ERR_INVALID
+    # a 512-token chunk of prefill for 8 sequences needs more than the array
+    need = lib.kvc_workspace_bytes(8, 512, 32, 8, 128, 4608, 0)
+    assert need > _lib.KVC_NOALLOC_SCRATCH_BYTES
+    assert na(T=512, N=32, L=4608) == E.KVC_ERR_WORKSPACE
+    # the decode and verify workloads fit
+    assert lib.kvc_workspace_bytes(64, 1, 32, 8, 128, 4097, 0) <= _lib.KVC_NOALLOC_SCRATCH_BYTES
+    assert lib.kvc_workspace_bytes(32, 5, 64, 8, 128, 8197, 0) <= _lib.KVC_NOALLOC_SCRATCH_BYTES
+    assert lib.kvc_workspace_bytes(32, 8, 64, 8, 128, 8200, 0) <= _lib.KVC_NOALLOC_SCRATCH_BYTES
+    assert na(B=0) == E.KVC_OK
