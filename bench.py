@@ -10,7 +10,14 @@ algorithmic bytes are the K and V rows each step must read:
 sum_b seq_len_b * 2 * K * H * elem_bytes. The default workload is batched
 decode (B=64, N=32, K=8, H=128, bf16, T=1, cached context U[512, 4096]).
 
-Prints ONE JSON line. ``--gpus`` above 1 is refused: this path runs on one GPU.
+roofline: the attention kernel alone, timed with HIP events on the stream it
+is launched on: the median over 20 samples of 20 back-to-back launches, cache
+replicas rotated so every launch reads from HBM rather than the 256 MB
+Infinity Cache. With the default workload the same kernel figures are also
+taken for the speculative-verify and paged long-context workloads
+(``other_workloads``), and a plain device copy is timed as a reference
+(``copy_probe``). Prints ONE JSON line. ``--gpus`` above 1 is refused: this
+path runs on one GPU.
 """
 
 from __future__ import annotations
@@ -55,6 +62,12 @@ def parse():
                    help="fused: one append_attend call per layer; separate: append, then attend")
     p.add_argument("--graph", action="store_true",
                    help="capture each replica's step in a HIP graph and replay it (launch-bound shapes)")
+    p.add_argument("--others", default="auto",
+                   help="comma-separated workloads whose attention kernel is also timed "
+                        "(auto: the verify and paged long-context workloads with the default "
+                        "workload; none: no others)")
+    p.add_argument("--samples", type=int, default=20, help="kernel timing samples (median)")
+    p.add_argument("--launches", type=int, default=20, help="back-to-back launches per sample")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only copy a MIB-mebibyte device buffer 10 times (known-size reference "
                         "for the HBM byte counters) and print its bandwidth")
@@ -176,13 +189,20 @@ def profiled_traffic(kernel: str, workload: str):
 
 def attn_flops(w, seq_lens) -> int:
     """Algorithmic flops of one step: for every new token and query head,
-    2 H for each visible key's q.k and 2 H for its p.v (causal inside the
-    block; with a window at most W keys; with a draft tree the tree's
-    ancestors among the new tokens, counted as causal here, an upper
-    bound)."""
+    2 H for each visible key's q.k and 2 H for its p.v. Visible keys: the
+    prior rows plus new tokens 0 .. t (causal inside the block), or with a
+    draft tree the prior rows plus t's ancestors and t itself; with a window
+    at most W keys."""
     rows = np.asarray(seq_lens, dtype=np.int64)
     t = np.arange(w.T, dtype=np.int64)
-    vis = rows[:, None] - w.T + t[None, :] + 1  # keys visible to new token t
+    if w.tree_parents:
+        from workloads import tree_mask_words
+
+        own = np.array([bin(int(x)).count("1") for x in tree_mask_words(w.tree_parents)],
+                       dtype=np.int64)
+    else:
+        own = t + 1
+    vis = rows[:, None] - w.T + own[None, :]  # keys visible to new token t
     if w.window:
         vis = np.minimum(vis, w.window)
     return int(vis.sum()) * w.N * w.H * 4
@@ -247,6 +267,141 @@ def cpu_baseline(w, prior, seed, budget_s):
     }
 
 
+def copy_probe(dev, mib=1024, samples=20):
+    """A plain device-to-device copy of ``mib`` MiB (torch's copy kernel),
+    median over ``samples``: the HBM read + write rate a simple streaming
+    kernel reaches on this GPU, as a reference beside the 8 TB/s peak."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    for _ in range(samples):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    del src, dst
+    return {"bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
+            "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "kind": "torch device copy, median of %d" % samples}
+
+
+def setup_workload(w, args, dev):
+    """Replicas of one workload's step on the GPU, enough that their K/V bytes
+    exceed twice the Infinity Cache (at least two)."""
+    from workloads import draw_prior_lengths
+
+    if w.prior_sweep:
+        prior = np.full(w.B, args.ctx, dtype=np.int64)
+    else:
+        prior = draw_prior_lengths(w.seed, w.B, w.prior_lo, w.prior_hi)
+    seq_lens = prior + w.T
+    step_bytes = kv_bytes(w, seq_lens)
+    if args.replicas > 0:
+        reps = args.replicas
+    else:
+        reps = max(2, math.ceil(2 * MALL_BYTES / max(1, step_bytes * w.layers)))
+        reps = min(reps, 4096)
+    log(f"bench: {w.name} ({w.description}); KV bytes/step {step_bytes * w.layers / 1e6:.1f} MB; "
+        f"{reps} replica(s) x {w.layers} layer(s)")
+    steps = [[Step(w, prior, w.seed * 1000 + r * w.layers + l, dev, args.num_workgroups)
+              for l in range(w.layers)] for r in range(reps)]
+    return steps, prior, seq_lens, step_bytes, reps
+
+
+def kernel_times(steps, one, reps, layers, stream, samples, launches):
+    """Per-launch milliseconds of the attention kernel: ``samples`` samples,
+    each ``launches`` back-to-back steps between two HIP events recorded on
+    the launch stream, divided by the launches (and layers) it holds."""
+    import torch
+
+    for i in range(reps):
+        for s in steps[i]:
+            one(s)
+    torch.cuda.synchronize()
+    out = []
+    k = 0
+    for _ in range(samples):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            for s in steps[k % reps]:
+                one(s)
+            k += 1
+        e1.record(stream)
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) / (launches * layers))
+    return out
+
+
+def roofline_of(w, kernel, seq_lens, step_bytes, times_ms, copy):
+    """The roofline object of one workload's attention kernel from its
+    per-launch time samples."""
+    attn_ms = float(np.median(times_ms))
+    achieved = step_bytes / (attn_ms * 1e-3) / 1e9
+    step_flops = attn_flops(w, seq_lens)
+    # bound: the matrix cores where the step's flops per K/V byte exceed their
+    # balance against HBM (a chunk of prefill), else HBM
+    mfma_bound = step_flops / step_bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    r = {
+        "kernel": kernel,
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": profiled_traffic(kernel, w.name),
+        "launch_ms": round(attn_ms, 5),
+        "launch_ms_min": round(float(np.min(times_ms)), 5),
+        "launch_ms_max": round(float(np.max(times_ms)), 5),
+        "timing": f"median of {len(times_ms)} samples (HIP events on the launch stream)",
+        "bytes_per_launch": step_bytes,
+    }
+    if copy:
+        r["pct_of_copy_probe"] = round(100 * achieved / copy["GBps_read_plus_write"], 2)
+    tflops = step_flops / (attn_ms * 1e-3) / 1e12
+    if kernel != "attn_valu_kernel" and not mfma_bound:
+        # a matrix-core kernel bound by HBM: its matrix-core use beside the
+        # HBM figure (algorithmic flops over the dense bf16/fp16 peak)
+        r.update({"flops_per_launch": step_flops, "mfma_tflops": round(tflops, 2),
+                  "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4)})
+    if mfma_bound:
+        r.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                  "flops_per_launch": step_flops, "hbm_GBps": round(achieved, 2)})
+    return r
+
+
+def plan_kernel(w, seq_lens, nwg):
+    import kv_cached_gqa_attention_amd as kvc
+
+    return kvc.plan_kernel(w.B, w.T, w.N, w.K, w.H, int(np.max(seq_lens)), nwg)
+
+
+def other_workload(name, args, dev, stream, copy):
+    """Kernel-only figures of another workload (same timing as the main one)."""
+    from workloads import get_workload
+
+    w = get_workload(name)
+    steps, prior, seq_lens, step_bytes, reps = setup_workload(w, args, dev)
+    kernel = plan_kernel(w, seq_lens, args.num_workgroups)
+    times = kernel_times(steps, lambda s: s.append_attend(), reps, w.layers, stream, args.samples,
+                         args.launches)
+    r = roofline_of(w, kernel, seq_lens, step_bytes, times, copy)
+    del steps
+    return {"workload": w.name, "description": w.description, "replicas": reps,
+            "mean_seq_len": float(np.mean(seq_lens)),
+            "tokens_per_s": round(w.B * w.T / (r["launch_ms"] * 1e-3), 1), "roofline": r}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -258,26 +413,15 @@ def main():
         return
     import torch
 
-    from workloads import draw_prior_lengths, get_workload
+    from workloads import get_workload
 
     w = get_workload(args.workload)
     dev = torch.device("cuda:0")
-    if w.prior_sweep:
-        prior = np.full(w.B, args.ctx, dtype=np.int64)
-    else:
-        prior = draw_prior_lengths(w.seed, w.B, w.prior_lo, w.prior_hi)
-    seq_lens = prior + w.T
-    step_bytes = kv_bytes(w, seq_lens)
+    stream = torch.cuda.current_stream(dev)
+    copy = copy_probe(dev)
+    log(f"bench: copy probe {copy['GBps_read_plus_write']} GB/s read+write")
+    steps, prior, seq_lens, step_bytes, reps = setup_workload(w, args, dev)
     layers = w.layers
-    if args.replicas > 0:
-        reps = args.replicas
-    else:
-        reps = max(1, math.ceil(2 * MALL_BYTES / max(1, step_bytes * layers)))
-        reps = min(reps, 4096)
-    log(f"bench: {w.name} ({w.description}); KV bytes/step {step_bytes * layers / 1e6:.1f} MB; "
-        f"{reps} replica(s) x {layers} layer(s)")
-    steps = [[Step(w, prior, w.seed * 1000 + r * layers + l, dev, args.num_workgroups) for l in range(layers)]
-             for r in range(reps)]
     torch.cuda.synchronize()
 
     def eager_step(i):
@@ -322,32 +466,13 @@ def main():
 
     # Attention kernel alone: back-to-back launches between two HIP events on
     # the stream the kernel runs on (torch's current stream is the one handed
-    # to the library), so the average is the kernel's own duration.
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # the dominant kernel: the fused call's attention kernel (its appends
-    # rewrite the same rows), or the attention kernel of the separate form
+    # to the library). The dominant kernel is the fused call's attention
+    # kernel (its appends rewrite the same rows), or the attention kernel of
+    # the separate form.
     one = (lambda s: s.append_attend()) if args.mode == "fused" else (lambda s: s.attend())
-    for i in range(reps):
-        for s in steps[i]:
-            one(s)
-    e0.record(stream)
-    for i in range(args.steps):
-        for s in steps[i % reps]:
-            one(s)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    attn_ms = e0.elapsed_time(e1) / (args.steps * layers)
-    achieved = step_bytes / (attn_ms * 1e-3) / 1e9
-    # bound: the matrix cores where the step's flops per K/V byte exceed their
-    # balance against HBM (a chunk of prefill), else HBM
-    step_flops = attn_flops(w, seq_lens)
-    mfma_bound = step_flops / step_bytes > MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    # the kernel that serves the workload's query blocks (as the library plans it)
-    rows = w.G * w.T
-    kernel = ("attn_wide_kernel" if rows > 64
-              else "attn_mfma_kernel" if rows > (8 if w.H == 64 else 4) else "attn_valu_kernel")
-    traffic = profiled_traffic(kernel, w.name)
+    times = kernel_times(steps, one, reps, layers, stream, args.samples, args.launches)
+    kernel = plan_kernel(w, seq_lens, args.num_workgroups)
+    roof = roofline_of(w, kernel, seq_lens, step_bytes, times, copy)
 
     value = step_bytes * layers / (ms_per_step * 1e-3) / 1e9
     tokens = w.B * w.T
@@ -382,36 +507,20 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
         "attention_steps_per_s": round(1e3 / ms_per_step, 1),
-        "roofline": {
-            "kernel": kernel,
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "launch_ms": round(attn_ms, 5),
-            "bytes_per_launch": step_bytes,
-        },
+        "roofline": roof,
+        "copy_probe": copy,
     }
-    tflops = step_flops / (attn_ms * 1e-3) / 1e12
-    if kernel != "attn_valu_kernel" and not mfma_bound:
-        # a matrix-core kernel bound by HBM: its matrix-core use beside the
-        # HBM figure (algorithmic flops over the dense bf16/fp16 peak)
-        result["roofline"].update({
-            "flops_per_launch": step_flops,
-            "mfma_tflops": round(tflops, 2),
-            "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-        })
-    if mfma_bound:
-        result["roofline"].update({
-            "bound": "mfma",
-            "achieved": round(tflops, 2),
-            "peak": MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-            "flops_per_launch": step_flops,
-        })
+    del steps, graphs
+    torch.cuda.synchronize()
+    others = args.others
+    if others == "auto":
+        others = "spec_verify_b32_t5,paged_long_b8" if w.name == "batched_decode_b64" else "none"
+    if others != "none":
+        torch.cuda.empty_cache()
+        result["other_workloads"] = []
+        for name in [x for x in others.split(",") if x]:
+            result["other_workloads"].append(other_workload(name, args, dev, stream, copy))
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(w, prior, w.seed, args.cpu_seconds)

@@ -295,6 +295,16 @@ kvc_status kvc_attn_noalloc(const kvc_cache *cache, const kvc_attn_options *opts
  */
 size_t kvc_workspace_bytes(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups);
 
+/*
+ * Host query: the name of the attention kernel a kvc_attn_verify call with
+ * these arguments (T = 1: kvc_attn_decode) launches, as the plan chooses it:
+ * "attn_valu_kernel" (few query rows per (b, k): vector ALUs),
+ * "attn_mfma_kernel" (up to 64 rows: matrix cores) or "attn_wide_kernel"
+ * (longer query blocks: matrix cores, units of 128 rows). A static string;
+ * NULL for invalid shapes. For reports and profiles; nothing is launched.
+ */
+const char *kvc_plan_kernel(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups);
+
 /* Host: a static, human-readable name for a status code. */
 const char *kvc_status_string(kvc_status status);
 

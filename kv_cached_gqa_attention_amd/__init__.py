@@ -15,6 +15,7 @@ from .api import (
     attend_noalloc,
     decode,
     gather,
+    plan_kernel,
     status_string,
     verify,
     workspace,
@@ -30,6 +31,7 @@ __all__ = [
     "attend_noalloc",
     "decode",
     "gather",
+    "plan_kernel",
     "status_string",
     "verify",
     "workspace",

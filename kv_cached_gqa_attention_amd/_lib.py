@@ -34,6 +34,7 @@ EXPORTS = (
     "kvc_attn",
     "kvc_attn_noalloc",
     "kvc_workspace_bytes",
+    "kvc_plan_kernel",
     "kvc_status_string",
     "kvc_gather",
 )
@@ -108,6 +109,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvc_attn_noalloc.restype = c_int
     lib.kvc_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int]
     lib.kvc_workspace_bytes.restype = c_size_t
+    lib.kvc_plan_kernel.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int]
+    lib.kvc_plan_kernel.restype = ctypes.c_char_p
     lib.kvc_status_string.argtypes = [c_int]
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_gather.argtypes = [cache_p, vp, vp, c_int, c_int, c_int, vp, c_int, vp]

@@ -116,6 +116,12 @@ def workspace_bytes(B, T, N, K, H, max_seq_len, num_workgroups=0) -> int:
     return int(_lib.load().kvc_workspace_bytes(B, T, N, K, H, max_seq_len, num_workgroups))
 
 
+def plan_kernel(B, T, N, K, H, max_seq_len, num_workgroups=0) -> str | None:
+    """Name of the attention kernel the library's plan picks for this shape."""
+    r = _lib.load().kvc_plan_kernel(B, T, N, K, H, max_seq_len, num_workgroups)
+    return None if r is None else r.decode()
+
+
 _ws_cache: dict = {}
 # Buffers replaced by a larger one stay referenced until the process ends: a
 # call still queued on the GPU (or a graph captured with an explicit buffer

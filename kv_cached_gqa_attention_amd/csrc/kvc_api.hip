@@ -410,6 +410,12 @@ size_t kvc_workspace_bytes(int B, int T, int N, int K, int H, int max_seq_len, i
   return p.bytes;
 }
 
+const char* kvc_plan_kernel(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups) {
+  Plan p;
+  if (!make_plan(B, T, N, K, H, max_seq_len, num_workgroups, &p)) return nullptr;
+  return p.wide ? "attn_wide_kernel" : p.mfma ? "attn_mfma_kernel" : "attn_valu_kernel";
+}
+
 const char* kvc_status_string(kvc_status status) {
   switch (status) {
     case KVC_OK: return "KVC_OK";

@@ -263,3 +263,17 @@ def test_noalloc_host_errors(lib):
     assert lib.kvc_workspace_bytes(32, 5, 64, 8, 128, 8197, 0) <= _lib.KVC_NOALLOC_SCRATCH_BYTES
     assert lib.kvc_workspace_bytes(32, 8, 64, 8, 128, 8200, 0) <= _lib.KVC_NOALLOC_SCRATCH_BYTES
     assert na(B=0) == E.KVC_OK
+
+
+def test_plan_kernel_names_the_kernel_by_rows(lib):
+    """Vector ALUs up to 4 query rows per (b, k) at H = 128 (8 at H = 64),
+    matrix cores up to 64 rows, units of 128 rows beyond."""
+    k = lambda *a: (lib.kvc_plan_kernel(*a) or b"").decode()
+    assert k(64, 1, 32, 8, 128, 4097, 0) == "attn_valu_kernel"   # G = 4
+    assert k(8, 1, 64, 8, 128, 4097, 0) == "attn_mfma_kernel"    # G = 8
+    assert k(8, 1, 16, 2, 64, 4097, 0) == "attn_valu_kernel"     # G = 8 at H = 64
+    assert k(32, 5, 64, 8, 128, 8197, 0) == "attn_mfma_kernel"   # 40 rows
+    assert k(32, 8, 64, 8, 128, 8200, 0) == "attn_mfma_kernel"   # 64 rows
+    assert k(8, 9, 64, 8, 128, 8200, 0) == "attn_wide_kernel"    # 72 rows
+    assert k(8, 512, 32, 8, 128, 4608, 0) == "attn_wide_kernel"
+    assert lib.kvc_plan_kernel(8, 1, 30, 8, 128, 4097, 0) is None  # N % K
