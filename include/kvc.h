@@ -305,8 +305,9 @@ size_t kvc_workspace_bytes(int B, int T, int N, int K, int H, int max_seq_len, i
  */
 const char *kvc_plan_kernel(int B, int T, int N, int K, int H, int max_seq_len, int num_workgroups);
 
-/* Host: a static, human-readable name for a status code. */
-const char *kvc_status_string(kvc_status status);
+/* Host: a static, human-readable name for a status code (any int: values
+ * that are not a kvc_status give "unknown kvc_status"). */
+const char *kvc_status_string(int status);
 
 /*
  * Test export: copy the first seq_lens[b] logical tokens of every sequence

@@ -10,7 +10,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvc.so")
+# KVC_LIB names another build of the same library (e.g. the host-sanitized
+# libkvc_asan.so for CPU-side checks); it must exist like the default.
+LIB_PATH = os.environ.get("KVC_LIB") or os.path.join(HERE, "libkvc.so")
 
 KVC_OK = 0
 KVC_ERR_INVALID = -1

@@ -416,7 +416,7 @@ const char* kvc_plan_kernel(int B, int T, int N, int K, int H, int max_seq_len, 
   return p.wide ? "attn_wide_kernel" : p.mfma ? "attn_mfma_kernel" : "attn_valu_kernel";
 }
 
-const char* kvc_status_string(kvc_status status) {
+const char* kvc_status_string(int status) {
   switch (status) {
     case KVC_OK: return "KVC_OK";
     case KVC_ERR_INVALID: return "KVC_ERR_INVALID: invalid argument";

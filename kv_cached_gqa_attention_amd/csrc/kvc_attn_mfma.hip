@@ -65,7 +65,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[2];
 
   build_tile_prefix(a, s_pre, s_wave);
-  fill_invalid<H>(a);
+  fill_invalid<H>(a, s_pre);
   const int worker = worker_of(a, blockIdx.x);
   const Partition part = make_partition(a, s_pre, worker);
   append_owned<H, THREADS, PAGED>(a, s_pre, part);

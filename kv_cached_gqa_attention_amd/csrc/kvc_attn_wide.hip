@@ -129,7 +129,7 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
 
   if (threadIdx.x < 16) s_bad[threadIdx.x] = 0;  // ordered by the barriers below
   build_tile_prefix(a, s_pre, s_wave);
-  fill_invalid<H>(a);
+  fill_invalid<H>(a, s_pre);
   const int worker = worker_of(a, blockIdx.x);
   const Partition part = make_partition(a, s_pre, worker);
   append_owned<H, THREADS, PAGED>(a, s_pre, part);

@@ -489,14 +489,16 @@ __device__ __forceinline__ void write_final(const AttnArgs& a, int b, int k, int
 }
 
 // NaN outputs for the rows of sequences with an invalid length. Units are
-// dealt round-robin to all launched workgroups.
+// dealt round-robin to all launched workgroups; lengths come from the LDS
+// copy build_tile_prefix made (s_pre[B + 1 + b]), so no global load is
+// waited for here.
 template <int H>
-__device__ __forceinline__ void fill_invalid(const AttnArgs& a) {
+__device__ __forceinline__ void fill_invalid(const AttnArgs& a, const int32_t* s_pre) {
   const float qnan = __int_as_float(0x7fc00000);
   const int units = a.B * a.K;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int b = u / a.K;
-    if (seq_valid(a.seq_lens[b], a.T, a.capacity)) continue;
+    if (seq_valid(s_pre[a.B + 1 + b], a.T, a.capacity)) continue;
     const int k = u - b * a.K;
     for (int e = threadIdx.x; e < a.R * H; e += THREADS) {
       const int r = e / H, h = e - (e / H) * H;
@@ -610,6 +612,18 @@ __device__ __forceinline__ void store_partial(const AttnArgs& a, const Segment& 
 
 // Count a stored partial (one thread, after its stores were acknowledged);
 // true for the unit's last one.
+//
+// Publication. A partial is written with device-coherent stores (agent-scope
+// atomic stores: on gfx950 they write through this XCD's L2 to the memory
+// side, which every XCD reads coherently) and the storing waves wait until
+// those stores are acknowledged (s_waitcnt vmcnt(0) counts a store as done
+// only once the coherent write has completed) before a barrier and this
+// count; the count itself is a device-scope atomic performed at the memory
+// side, so it is ordered after the acknowledged partial. The workgroup whose
+// count completes a unit takes a device-scope acquire fence and reads the
+// partials with device-coherent loads. A release on every count (a write-back
+// of the whole L2 per workgroup) measured 15% slower on batched decode, so
+// the producer side relies on the acknowledgment instead.
 __device__ __forceinline__ bool count_partial(const AttnArgs& a, const Segment& s) {
   const int prev = __hip_atomic_fetch_add(&a.counters[s.unit], 1, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
@@ -774,6 +788,9 @@ __device__ __forceinline__ void count_and_merge(const AttnArgs& a, const SharedU
   if (threadIdx.x == 0) {
     const bool f0 = count_partial(a, sh.s0);
     const bool f1 = sh.n > 1 && count_partial(a, sh.s1);
+    // the merger: acquire the other workgroups' partials (the barrier below
+    // orders this before every thread's merge loads)
+    if (f0 || f1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     s_flag[0] = f0;
     s_flag[1] = f1;
   }
