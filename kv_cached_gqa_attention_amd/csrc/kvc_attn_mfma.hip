@@ -52,6 +52,10 @@ template <bool BF, int H, int NB, bool PAGED, bool MASKED, bool QLDS>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(QLDS ? 2 : 1, QLDS ? 2 : 1)))
 void attn_mfma_kernel(AttnArgs a, int nslots) {
   constexpr int RMAX = NB * 16;  // query rows per unit (row block)
+  // Row stride (floats) of the waves' fold in LDS: H + 4 puts the 16 query
+  // rows one fold write touches (one per lane of a 16-lane group) in
+  // distinct banks (a stride of H sent all 16 to one bank).
+  constexpr int OST = H + 4;
   constexpr int KS = H / 32;     // k-steps of S^T over h
   constexpr int MH = H / 16;     // 16-row h blocks of O^T
   constexpr int ROWB = H * 2;
@@ -61,7 +65,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   // [2B + 1], (QLDS: the unit's query rows,) then the slots
   extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];
   __shared__ float s_m[RMAX], s_l[RMAX];
-  __shared__ float s_o_own[QLDS ? 4 : RMAX * H];
+  __shared__ float s_o_own[QLDS ? 4 : RMAX * OST];
   __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[2];
 
   build_tile_prefix(a, s_pre, s_wave);
@@ -373,7 +377,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
           for (int mh = 0; mh < MH; ++mh)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              float* dst = &s_o[col * H + mh * 16 + 4 * g + i];
+              float* dst = &s_o[col * OST + mh * 16 + 4 * g + i];
               *dst = (w > 0 ? *dst * sp : 0.f) + ot[mh][nb][i] * sw;
             }
           if (g == 0) {
@@ -387,7 +391,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    finish_segment<H, 1>(a, s, worker, s_m, s_l, s_o, s_m, segbad, shared);
+    finish_segment<H, 1, OST>(a, s, worker, s_m, s_l, s_o, s_m, segbad, shared);
     if (cs.x + 1 >= part.hi) break;
     cs.advance(a, s_pre, part);
   }

@@ -546,27 +546,28 @@ __device__ __forceinline__ void combine_rows(const AttnArgs& a, int rows, const 
   }
 }
 
-// Combined state of the NW waves for (row r, dim h), after combine_rows.
-template <int H, int NW>
+// Combined state of the NW waves for (row r, dim h), after combine_rows;
+// rows of s_o are OST floats apart.
+template <int H, int NW, int OST = H>
 __device__ __forceinline__ void combine_waves(const AttnArgs& a, const float* s_m, const float* s_l,
                                               const float* s_o, const float* s_w, int r, int h,
                                               float& M, float& L, float& O) {
   if constexpr (NW == 1) {
     M = s_m[r];
     L = s_l[r];
-    O = s_o[r * H + h];
+    O = s_o[r * OST + h];
   } else {
     M = s_w[NW * a.RMAX + r];
     L = s_w[(NW + 1) * a.RMAX + r];
     O = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) O += s_w[w * a.RMAX + r] * s_o[(w * a.RMAX + r) * H + h];
+    for (int w = 0; w < NW; ++w) O += s_w[w * a.RMAX + r] * s_o[(w * a.RMAX + r) * OST + h];
   }
 }
 
 // The segment is its whole unit: write the output. Ends with a barrier, so
 // LDS may be reused afterwards.
-template <int H, int NW>
+template <int H, int NW, int OST = H>
 __device__ __forceinline__ void finish_direct(const AttnArgs& a, const Segment& s, const float* s_m,
                               const float* s_l, const float* s_o, float* s_w, bool bad) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
@@ -576,7 +577,7 @@ __device__ __forceinline__ void finish_direct(const AttnArgs& a, const Segment& 
   for (int e = threadIdx.x; e < rows * H; e += THREADS) {
     const int r = e / H, h = e - (e / H) * H;
     float M, L, O;
-    combine_waves<H, NW>(a, s_m, s_l, s_o, s_w, r, h, M, L, O);
+    combine_waves<H, NW, OST>(a, s_m, s_l, s_o, s_w, r, h, M, L, O);
     if (bad) O = L = M = qnan;
     write_final(a, s.b, s.k, row0 + r, H, h, O, M, L);
   }
@@ -587,7 +588,7 @@ __device__ __forceinline__ void finish_direct(const AttnArgs& a, const Segment& 
 // (they bypass this XCD's L2 copy); they are waited for in count_and_merge,
 // before the partial is counted. Ends with a barrier, so LDS may be reused
 // afterwards.
-template <int H, int NW>
+template <int H, int NW, int OST = H>
 __device__ __forceinline__ void store_partial(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
                               const float* s_l, const float* s_o, float* s_w, bool bad) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
@@ -599,7 +600,7 @@ __device__ __forceinline__ void store_partial(const AttnArgs& a, const Segment& 
   for (int e = threadIdx.x; e < rows * H; e += THREADS) {
     const int r = e / H, h = e - (e / H) * H;
     float M, L, O;
-    combine_waves<H, NW>(a, s_m, s_l, s_o, s_w, r, h, M, L, O);
+    combine_waves<H, NW, OST>(a, s_m, s_l, s_o, s_w, r, h, M, L, O);
     if (bad) O = L = M = qnan;
     store_coherent(po + r * H + h, O);
     if (h == 0) {
@@ -631,29 +632,44 @@ __device__ __forceinline__ bool count_partial(const AttnArgs& a, const Segment& 
 }
 
 // Merge all partials of the unit and write the output; called by the
-// workgroup that counted the last one. Every other partial was acknowledged
-// before its count, which preceded ours; device-coherent loads see them. The
-// count is reset for the next call.
+// workgroup that counted the last one, after its acquire fence. The count is
+// reset for the next call.
 //
 // With LDS scratch for every partial's row statistics (n * rows * 2 floats
-// within `cap`) and rows * H <= EPT * THREADS, the merge takes 1 + n memory
-// round trips: the statistics of all partials at once (each row's weights
-// computed once, into the scratch), then per partial one load for each of
-// the thread's EPT output elements, all in flight together. Otherwise the
-// partials are folded in chunks of 8 whose loads are issued together, with
-// an online rescale between chunks.
+// within `cap`) and rows * H <= EPT * THREADS, the thread's EPT output
+// elements are merged in passes of EP; a pass loads PJ partials' elements at
+// once (one memory round trip per PJ partials, PJ * EP <= 32 registers), and
+// the first of these loads is issued together with the statistics of all
+// partials (into the scratch, each row's weights computed once). Otherwise
+// the partials are folded in chunks of 8 whose loads are issued together,
+// with an online rescale between chunks.
 template <int H, int EPT>
 __device__ __forceinline__ void merge_partials(const AttnArgs& a, const Segment& s, float* scratch, int cap) {
   const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);
   const int row0 = s.rb * a.RMAX;
   constexpr int CH = 8;
+  constexpr int EP = EPT < 16 ? EPT : 16;
+  constexpr int PJ = 32 / EP > 16 ? 16 : 32 / EP;
   const int n = s.n_parts;
   auto slot_of = [&](int j) { return (int64_t)s.first_wg + j + s.unit; };
   if (n * rows * 2 + 2 * rows <= cap && rows * H <= EPT * THREADS) {
     float* sw = scratch;                // [n][rows]: m, then the weight 2^(m - M)
     float* sl = scratch + n * rows;     // [n][rows]: l
-    float* sM = scratch + 2 * n * rows; // [rows]: M, then 1 / L... (M and L)
-    float* sL = sM + rows;
+    float* sM = scratch + 2 * n * rows; // [rows]: M
+    float* sL = sM + rows;              // [rows]: L
+    // element u of pass p0: threadIdx.x + (p0 + u) * THREADS, clamped into
+    // the unit (the duplicates are loaded and never stored)
+    auto elem = [&](int p0, int u) { return min((int)threadIdx.x + (p0 + u) * THREADS, rows * H - 1); };
+    float ov[PJ][EP];
+    auto load_o = [&](int p0, int j0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jj = 0; jj < PJ; ++jj) {
+        const float* po = a.part_o + slot_of(min(j0 + jj, n - 1)) * a.RMAX * H;
+#pragma unroll
+        for (int u = 0; u < EP; ++u) ov[jj][u] = load_coherent(po + elem(p0, u));
+      }
+    };
+    load_o(0, 0);
     for (int e = threadIdx.x; e < n * rows; e += THREADS) {
       const int j = e / rows, r = e - (e / rows) * rows;
       const float* ml = a.part_ml + slot_of(j) * a.RMAX * 2 + r * 2;
@@ -674,26 +690,19 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, const Segment&
       sL[r] = L;
     }
     __syncthreads();
-    // each thread's EPT elements in passes of up to 16, one partial at a
-    // time: per partial, a pass's loads are all in flight together
-    constexpr int EP = EPT < 16 ? EPT : 16;
 #pragma unroll
     for (int p0 = 0; p0 < EPT; p0 += EP) {
       float O[EP];
 #pragma unroll
       for (int u = 0; u < EP; ++u) O[u] = 0.f;
-      for (int j = 0; j < n; ++j) {
-        const float* po = a.part_o + slot_of(j) * a.RMAX * H;
-        float o[EP];
+      for (int j0 = 0; j0 < n; j0 += PJ) {
+        if (p0 > 0 || j0 > 0) load_o(p0, j0);
 #pragma unroll
-        for (int u = 0; u < EP; ++u) {
-          const int e = min((int)threadIdx.x + (p0 + u) * THREADS, rows * H - 1);
-          o[u] = load_coherent(po + e);
-        }
+        for (int jj = 0; jj < PJ; ++jj) {
+          if (j0 + jj < n) {
 #pragma unroll
-        for (int u = 0; u < EP; ++u) {
-          const int e = min((int)threadIdx.x + (p0 + u) * THREADS, rows * H - 1);
-          O[u] += sw[j * rows + e / H] * o[u];
+            for (int u = 0; u < EP; ++u) O[u] += sw[(j0 + jj) * rows + elem(p0, u) / H] * ov[jj][u];
+          }
         }
       }
 #pragma unroll
@@ -762,14 +771,14 @@ struct SharedUnits {
 
 // Finish a segment: the output, or a partial to be counted at the worker's
 // end. Ends with a barrier, so LDS may be reused afterwards.
-template <int H, int NW>
+template <int H, int NW, int OST = H>
 __device__ __forceinline__ void finish_segment(const AttnArgs& a, const Segment& s, int worker, const float* s_m,
                                const float* s_l, const float* s_o, float* s_w, bool bad,
                                SharedUnits& sh) {
   if (s.n_parts == 1) {
-    finish_direct<H, NW>(a, s, s_m, s_l, s_o, s_w, bad);
+    finish_direct<H, NW, OST>(a, s, s_m, s_l, s_o, s_w, bad);
   } else {
-    store_partial<H, NW>(a, s, worker, s_m, s_l, s_o, s_w, bad);
+    store_partial<H, NW, OST>(a, s, worker, s_m, s_l, s_o, s_w, bad);
     sh.add(s);
   }
 }
