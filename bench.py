@@ -128,10 +128,10 @@ class Step:
         self.opts = bool(w.window or w.tree_parents)
         self.tree = None
         if w.tree_parents:
-            from workloads import tree_mask_words
+            from workloads import tree_mask_rows
 
-            words = tree_mask_words(w.tree_parents).view(np.int32)
-            self.tree = torch.from_numpy(np.tile(words, (w.B, 1))).to(dev)
+            rows = tree_mask_rows(w.tree_parents).view(np.int32)  # [T, (T + 31) // 32]
+            self.tree = torch.from_numpy(np.ascontiguousarray(np.tile(rows[None], (w.B, 1, 1)))).to(dev)
 
     def append(self):
         self.kvc.append(self.cache, self.inp.k_new, self.inp.v_new, self.seq_lens)
@@ -196,9 +196,9 @@ def attn_flops(w, seq_lens) -> int:
     rows = np.asarray(seq_lens, dtype=np.int64)
     t = np.arange(w.T, dtype=np.int64)
     if w.tree_parents:
-        from workloads import tree_mask_words
+        from workloads import tree_mask_rows
 
-        own = np.array([bin(int(x)).count("1") for x in tree_mask_words(w.tree_parents)],
+        own = np.array([sum(bin(int(x)).count("1") for x in row) for row in tree_mask_rows(w.tree_parents)],
                        dtype=np.int64)
     else:
         own = t + 1

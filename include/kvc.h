@@ -80,6 +80,9 @@ typedef enum { KVC_F16 = 0, KVC_BF16 = 1, KVC_F32 = 2 } kvc_dtype;
 /* Largest number of new tokens per sequence in one attention call. */
 #define KVC_MAX_T 2048
 
+/* Largest number of new tokens per sequence with a draft-tree mask. */
+#define KVC_MAX_TREE_T 256
+
 /*
  * One layer's key cache and value cache (same layout, same dtype).
  *
@@ -226,13 +229,15 @@ kvc_status kvc_append_attend(const kvc_cache *cache, const void *k_new, const vo
  *   ("Stanford CS336 Day 13 - Inference", "Local Attention": rows that left
  *   the window can leave the cache).
  * tree_mask: NULL for the causal rule inside the block, or device
- *   [B, T] uint32 words for draft-tree verification ("Accelerating Sonar
- *   through speculation", section "EAGLE": tree-shaped drafts are verified
- *   with custom attention masks): new token t of sequence b sees new token u
- *   exactly when bit u of tree_mask[b * T + t] is set (set t's own bit and
- *   its ancestors'); every prior row stays visible; bits >= T are ignored.
- *   4-byte aligned; T <= 32. A query that sees no key at all gets NaN.
- *   Both options compose: a key must pass both rules.
+ *   [B, T, TW] uint32 words, TW = (T + 31) / 32, for draft-tree verification
+ *   ("Accelerating Sonar through speculation", section "EAGLE": tree-shaped
+ *   drafts are verified with custom attention masks): the TW words of (b, t)
+ *   are a T-bit row, bit u in word u / 32 at bit u % 32; new token t of
+ *   sequence b sees new token u exactly when bit u of its row is set (set
+ *   t's own bit and its ancestors'); every prior row stays visible; bits
+ *   >= T are ignored. With T <= 32 this is one word per token, [B, T].
+ *   4-byte aligned; T <= KVC_MAX_TREE_T. A query that sees no key at all
+ *   gets NaN. Both options compose: a key must pass both rules.
  * k_new, v_new: NULL, or the new rows to append first, as kvc_append_attend.
  * reserved: must be 0.
  */
@@ -251,7 +256,7 @@ typedef struct {
  * K, H, max_seq_len and num_workgroups is always enough (a window only
  * lowers the need). Errors: as kvc_attn_verify and kvc_append_attend, plus
  * KVC_ERR_INVALID for window < 0, reserved != 0, a misaligned tree_mask or a
- * tree_mask with T > 32.
+ * tree_mask with T > KVC_MAX_TREE_T.
  */
 kvc_status kvc_attn(const kvc_cache *cache, const kvc_attn_options *opts, const void *q, void *out,
                     int out_dtype, float *lse, int B, int T, int N, int K, int H,

@@ -267,9 +267,10 @@ def attend(q, cache: Cache, seq_lens, max_seq_len, window=0, tree_mask=None, k_n
 
     q: [B, N, H] (one new token) or [B, T, N, H]. window: 0 or the number of
     most recent positions each new token sees (itself included). tree_mask:
-    None (causal inside the block) or int32 [B, T] words, bit u of word
-    (b, t) = new token t sees new token u. k_new, v_new: optional rows to
-    append first ([B, T, K, H]).
+    None (causal inside the block) or int32 [B, T, (T + 31) // 32] mask
+    rows ([B, T] for T <= 32): bit u of row (b, t), in word u // 32, set =
+    new token t sees new token u. k_new, v_new: optional rows to append
+    first ([B, T, K, H]).
     """
     if q.dim() not in (3, 4):
         raise ValueError("attend takes q [B, N, H] or [B, T, N, H]")
@@ -277,11 +278,7 @@ def attend(q, cache: Cache, seq_lens, max_seq_len, window=0, tree_mask=None, k_n
     opts = _lib.KvcAttnOptions()
     opts.window = int(window)
     if tree_mask is not None:
-        _gpu(tree_mask, "tree_mask")
-        if tree_mask.dtype != torch.int32 or tuple(tree_mask.shape) != (q.shape[0], T):
-            raise ValueError("tree_mask must be int32 [B, T]")
-        if not tree_mask.is_contiguous():
-            raise ValueError("tree_mask must be contiguous")
+        _check_tree_mask(tree_mask, q.shape[0], T)
         opts.tree_mask = _ptr(tree_mask)
     if (k_new is None) != (v_new is None):
         raise ValueError("give both k_new and v_new, or neither")
@@ -325,9 +322,7 @@ def attend_noalloc(q, cache: Cache, seq_lens, max_seq_len, out, lse=None, window
     opts = _lib.KvcAttnOptions()
     opts.window = int(window)
     if tree_mask is not None:
-        _gpu(tree_mask, "tree_mask")
-        if tree_mask.dtype != torch.int32 or tuple(tree_mask.shape) != (B, T) or not tree_mask.is_contiguous():
-            raise ValueError("tree_mask must be contiguous int32 [B, T]")
+        _check_tree_mask(tree_mask, B, T)
         opts.tree_mask = _ptr(tree_mask)
     if (k_new is None) != (v_new is None):
         raise ValueError("give both k_new and v_new, or neither")
@@ -346,6 +341,18 @@ def attend_noalloc(q, cache: Cache, seq_lens, max_seq_len, out, lse=None, window
                                       int(num_workgroups), _stream(q.device))
     _check(st, "kvc_attn_noalloc")
     return out
+
+
+def _check_tree_mask(tree_mask, B, T):
+    """int32 [B, T, (T + 31) // 32] mask rows (bit u of a row in word u // 32),
+    or [B, T] when one word per token suffices (T <= 32)."""
+    _gpu(tree_mask, "tree_mask")
+    tw = (T + 31) // 32
+    shapes = {(B, T, tw)} | ({(B, T)} if tw == 1 else set())
+    if tree_mask.dtype != torch.int32 or tuple(tree_mask.shape) not in shapes:
+        raise ValueError(f"tree_mask must be int32 [B, T, {tw}]" + (" or [B, T]" if tw == 1 else ""))
+    if not tree_mask.is_contiguous():
+        raise ValueError("tree_mask must be contiguous")
 
 
 def gather(cache: Cache, seq_lens, max_seq_len):

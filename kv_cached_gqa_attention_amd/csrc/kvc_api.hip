@@ -254,7 +254,7 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   const kvc_status st = check_cache(c, K, H, &capacity, &shift);
   if (st != KVC_OK) return st;
   if (B < 0 || T < 1 || T > KVC_MAX_T || N < 1 || N % K || num_wg < 0) return KVC_ERR_INVALID;
-  if (tree && T > 32) return KVC_ERR_INVALID;  // one 32-bit mask word per new token
+  if (tree && T > KVC_MAX_TREE_T) return KVC_ERR_INVALID;  // (T + 31) / 32 mask words per new token
   if (out_dtype != KVC_F16 && out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
   if (max_seq_len < T || max_seq_len > capacity) return KVC_ERR_INVALID;
   if (!isfinite(scale)) return KVC_ERR_INVALID;
@@ -313,6 +313,7 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   a.scale_log2 = scale * 1.4426950408889634f;
   a.window = window;
   a.tree = tree;
+  a.tree_words = (T + 31) / 32;
   char* w = static_cast<char*>(ws);
   a.counters = reinterpret_cast<int32_t*>(w);
   a.part_ml = reinterpret_cast<float*>(w + p.off_ml);

@@ -178,7 +178,8 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
     // Q^T fragments (B operand): query row rb*RMAX + 16 nb + c, h = 32 ks + 8 g + j.
     uint4 qf[QLDS ? 1 : NB][KS];
     int tq[NB];         // new-token index of this lane's query column
-    uint32_t tw[NB];    // its tree word
+    // its tree-mask row: T <= RMAX <= 64 new tokens, so at most two words
+    uint32_t tw[NB], tw1[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int rr = s.rb * RMAX + nb * 16 + c;
@@ -196,7 +197,9 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
         }
         tq[nb] = a.T - 1;  // padding column: any valid row, discarded
       }
-      tw[nb] = MASKED && a.tree ? a.tree[(int64_t)s.b * a.T + tq[nb]] : 0u;
+      const uint32_t* trow = MASKED && a.tree ? a.tree + ((int64_t)s.b * a.T + tq[nb]) * a.tree_words : nullptr;
+      tw[nb] = trow ? trow[0] : 0u;
+      tw1[nb] = trow && a.tree_words > 1 ? trow[1] : 0u;
     }
     // Every outstanding load (these and the copies in flight) has landed,
     // so no wait for the query loads falls inside the tile loop.
@@ -277,7 +280,8 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
           for (int i = 0; i < 4; ++i) {
             float v = st[mb][nb][i] * a.scale_log2;
             const int tok = tok0 + mb * 16 + 4 * g + i;
-            if (edge && !(MASKED ? key_visible(a, tok, new0, tq[nb], tw[nb]) : tok <= new0 + tq[nb]))
+            if (edge && !(MASKED ? key_visible(a, tok, new0, tq[nb], tok - new0 >= 32 ? tw1[nb] : tw[nb])
+                                 : tok <= new0 + tq[nb]))
               v = -__builtin_inff();
             p[nb][mb][i] = v;
           }

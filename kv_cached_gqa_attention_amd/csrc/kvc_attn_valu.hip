@@ -132,7 +132,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     uint32_t tword[R];
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      tword[r] = MASKED && a.tree ? load_uniform(a.tree, (int64_t)g.b * a.T + r / a.G) : 0u;
+      // (here T <= R <= 8: every new token's bit is in word 0 of its row)
+      tword[r] = MASKED && a.tree ? load_uniform(a.tree, ((int64_t)g.b * a.T + r / a.G) * a.tree_words) : 0u;
 
     float m[R], l[R], o[R][DPL];
 #pragma unroll

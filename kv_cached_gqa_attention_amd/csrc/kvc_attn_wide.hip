@@ -22,6 +22,7 @@
 // ring of `nslots` halves (K and V tiles alternating), all but the tile in
 // use in flight. Every wave computes every live tile of the unit; the key
 // mask is evaluated only on tiles not wholly visible to its rows.
+#include "kvc.h"
 #include "kvc_device.h"
 #include "kvc_dma.h"
 #include "kvc_internal.h"
@@ -32,6 +33,17 @@ namespace kvc {
 namespace {
 
 constexpr int NB = 2;                // 16-row blocks per wave
+constexpr int TREE_WORDS = KVC_MAX_TREE_T / 32;  // mask words per row
+
+// The word of a tree-mask row holding the bit of new token u (u >= 0; an
+// index past the row gives a word that is never consulted).
+__device__ __forceinline__ uint32_t tree_word(const uint32_t (&row)[TREE_WORDS], int u) {
+  const int w = u >> 5;
+  uint32_t v = row[0];
+#pragma unroll
+  for (int i = 1; i < TREE_WORDS; ++i) v = w == i ? row[i] : v;
+  return v;
+}
 constexpr int RW = NB * 16;          // query rows per wave
 constexpr int MAX_SLOTS = 8;         // ring halves (waits are counted up to this)
 constexpr int MIN_SLOTS = 4;         // a tile in use and the next one in flight
@@ -210,12 +222,14 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
     const int row0w = s.rb * a.RMAX + wave * RW;  // this wave's first row of the unit
     const int tq_lo = min(row0w, a.R - 1) / a.G;  // its first new token
     int tq[NB];         // new-token index of this lane's query column
-    uint32_t tw[NB];    // its tree word
+    uint32_t tw[NB][TREE_WORDS];  // its tree-mask row (T <= KVC_MAX_TREE_T)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int rr = row0w + nb * 16 + c;
       tq[nb] = rr < a.R ? rr / a.G : a.T - 1;  // padding column: any valid row, discarded
-      tw[nb] = MASKED && a.tree ? a.tree[(int64_t)s.b * a.T + tq[nb]] : 0u;
+      const uint32_t* trow = MASKED && a.tree ? a.tree + ((int64_t)s.b * a.T + tq[nb]) * a.tree_words : nullptr;
+#pragma unroll
+      for (int w = 0; w < TREE_WORDS; ++w) tw[nb][w] = trow && w < a.tree_words ? trow[w] : 0u;
     }
     // this wave's query rows into its LDS rows (rows past R repeat row R - 1;
     // their columns are discarded); only this wave reads them
@@ -297,7 +311,8 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int tok = tok0 + mb * 16 + 4 * g + i;
-                if (!(MASKED ? key_visible(a, tok, new0, tq[nb], tw[nb]) : tok <= new0 + tq[nb]))
+                if (!(MASKED ? key_visible(a, tok, new0, tq[nb], tree_word(tw[nb], tok - new0))
+                             : tok <= new0 + tq[nb]))
                   p[nb][mb][i] = -__builtin_inff();
               }
         }

@@ -81,7 +81,8 @@ struct AttnArgs {
   // positions (0: none), and per (b, t) a mask word over the T new rows
   // (nullptr: causal inside the block). See unit_first_step and key_visible.
   int32_t window;
-  const uint32_t* tree;  // [B, T]
+  const uint32_t* tree;  // [B, T, tree_words]
+  int32_t tree_words;    // mask words per new token: (T + 31) / 32
 };
 
 // ---------------------------------------------------------------- dtypes
@@ -258,9 +259,10 @@ __device__ __forceinline__ int first_visible(const AttnArgs& a, int len) {
 }
 
 // Whether key position tok is visible to new token t of a sequence whose new
-// rows start at new0 (= seq_len - T), given that token's tree word (ignored
-// without a tree mask). Prior rows are visible, new rows by the causal rule
-// or the tree word, rows past the sequence never; a window further requires
+// rows start at new0 (= seq_len - T), given the word of t's tree-mask row
+// that holds the key's bit (word (tok - new0) / 32; ignored without a tree
+// mask). Prior rows are visible, new rows by the causal rule or the tree
+// row, rows past the sequence never; a window further requires
 // tok > new0 + t - W.
 __device__ __forceinline__ bool key_visible(const AttnArgs& a, int tok, int new0, int t,
                                             uint32_t word) {
@@ -268,7 +270,7 @@ __device__ __forceinline__ bool key_visible(const AttnArgs& a, int tok, int new0
   if (tok < new0)
     ok = true;
   else if (a.tree)
-    ok = tok - new0 < a.T && ((word >> (tok - new0)) & 1u);
+    ok = tok - new0 < a.T && ((word >> ((tok - new0) & 31)) & 1u);
   else
     ok = tok <= new0 + t;
   if (a.window > 0) ok = ok && tok > new0 + t - a.window;

@@ -68,7 +68,7 @@ def run_case(B, T, N, K, H, dtype, prior, layout="contiguous", seed=1, num_workg
         q = inp.q[:, 0].contiguous() if T == 1 else inp.q
         tm = None
         if tree is not None:
-            tm = torch.tensor(np.asarray(tree, dtype=np.uint32).view(np.int32), device=device)
+            tm = torch.from_numpy(pack_tree_rows(tree, T)).to(device)
         kw = dict(k_new=inp.k_new, v_new=inp.v_new) if fused else {}
         if not fused:
             kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
@@ -99,6 +99,18 @@ def run_case(B, T, N, K, H, dtype, prior, layout="contiguous", seed=1, num_workg
                               num_workgroups=num_workgroups, return_lse=True)
     torch.cuda.synchronize()
     return Run(inp, cache, seq_lens, out, lse, scale, table)
+
+
+def pack_tree_rows(tree, T):
+    """Per sequence T mask rows given as Python ints (bit u = sees new token
+    u) -> int32 [B, T, (T + 31) // 32], bit u in word u // 32."""
+    tw = (T + 31) // 32
+    rows = np.zeros((len(tree), T, tw), dtype=np.uint32)
+    for b, words in enumerate(tree):
+        for t, m in enumerate(words):
+            for w in range(tw):
+                rows[b, t, w] = (int(m) >> (32 * w)) & 0xFFFFFFFF
+    return rows.view(np.int32)
 
 
 def to_device(inp, device):

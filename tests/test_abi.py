@@ -223,7 +223,8 @@ def test_attn_options_layout_and_errors(lib):
     assert at(reserved=3) == E.KVC_ERR_INVALID
     assert at(tree=FAKE + 2) == E.KVC_ERR_INVALID
     assert at(T=2049) == E.KVC_ERR_INVALID
-    assert at(T=33, tree=FAKE) == E.KVC_ERR_INVALID  # one 32-bit mask word per new token
+    assert at(T=257, tree=FAKE) == E.KVC_ERR_INVALID  # mask rows up to KVC_MAX_TREE_T tokens
+    assert at(B=0, T=256, tree=FAKE) == E.KVC_OK
     assert at(ws=None) == E.KVC_ERR_WORKSPACE
     assert at(B=0) == E.KVC_OK
     assert at(B=0, opts=False) == E.KVC_OK

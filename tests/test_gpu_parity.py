@@ -708,3 +708,46 @@ def test_default_workspace_is_per_stream_and_refused_under_capture(gpu_device):
         with torch.cuda.graph(g, stream=side):
             kvc.decode(q, run.cache, run.seq_lens, int(inp.seq_lens.max()))
     torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------- draft trees of more than 32 tokens
+
+LONG_TREES = [
+    # B, T, N, K, H, dtype, prior       kernel (rows per (b, k))
+    (2, 33, 8, 8, 128, BF, [90, 700]),    # matrix cores, 33 rows: two mask words
+    (2, 64, 4, 4, 64, HF, [0, 300]),      # matrix cores, 64 rows, empty prior context
+    (2, 40, 16, 8, 128, BF, [500, 17]),   # 80 rows: units of 128 rows
+    (1, 100, 8, 4, 128, BF, [250]),       # 200 rows: two row blocks, four words
+    (1, 256, 4, 4, 64, HF, [64]),         # 256 tokens: the longest tree, eight words
+]
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("case", LONG_TREES, ids=_ids(LONG_TREES))
+def test_draft_tree_longer_than_32_tokens(gpu_device, case, layout):
+    B, T, N, K, H, dtype, prior = case
+    rng = np.random.default_rng(700 + T)
+    words = _random_tree_words(rng, B, T)
+    run = run_case(B, T, N, K, H, dtype, prior, layout=layout, seed=701 + T, tree=words)
+    compare_units(run, all_units(run.inp))
+
+
+@pytest.mark.parametrize("case", LONG_TREES[:4], ids=_ids(LONG_TREES[:4]))
+def test_long_causal_tree_rows_are_the_plain_verify(gpu_device, case):
+    from oracle import causal_tree_words
+
+    B, T, N, K, H, dtype, prior = case
+    kw = dict(seed=710, num_workgroups=17)
+    plain = run_case(B, T, N, K, H, dtype, prior, **kw)
+    tree = run_case(B, T, N, K, H, dtype, prior, tree=[causal_tree_words(T)] * B, **kw)
+    assert torch.equal(plain.out, tree.out) and torch.equal(plain.lse, tree.lse)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_long_tree_with_window(gpu_device, fused):
+    B, T, N, K, H = 2, 48, 8, 4, 128
+    rng = np.random.default_rng(720)
+    words = _random_tree_words(rng, B, T)
+    run = run_case(B, T, N, K, H, BF, [300, 33], seed=721, tree=words, window=70, fused=fused,
+                   layout="paged", block_size=8)
+    compare_units(run, all_units(run.inp))

@@ -100,3 +100,20 @@ def test_tree_mask_words_agree_with_the_oracle_reading():
     for parents in ([-1], [-1, 0, 1, 2], [-1, 0, 0, 0, 0], [-1, 0, 0, 1, 1, 2, 2, 3], [-1, -1, 1, 0],
                     WORKLOADS["tree_verify_b32_t8"].tree_parents):
         assert [int(x) for x in tree_mask_words(list(parents))] == ancestor_words(list(parents))
+
+
+def test_tree_mask_rows_agree_with_the_oracle_reading_for_long_blocks():
+    """Rows of several 32-bit words (T up to 256): bit u of row t, in word
+    u // 32, is bit u of the oracle's ancestor mask."""
+    from oracle import ancestor_words
+    from workloads import tree_mask_rows
+
+    rng = np.random.default_rng(5)
+    for T in (1, 31, 32, 33, 64, 100, 256):
+        parents = [-1] + [int(rng.integers(-1, u)) for u in range(1, T)]
+        rows = tree_mask_rows(parents)
+        assert rows.shape == (T, (T + 31) // 32) and rows.dtype == np.uint32
+        ref = ancestor_words(parents)
+        for t in range(T):
+            got = sum(int(rows[t, w]) << (32 * w) for w in range(rows.shape[1]))
+            assert got == ref[t], (T, t)

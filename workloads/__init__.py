@@ -15,6 +15,7 @@ from .synth import (
     layout_paged,
     logical_kv,
     make_block_table,
+    tree_mask_rows,
     tree_mask_words,
 )
 
@@ -29,5 +30,6 @@ __all__ = [
     "layout_paged",
     "logical_kv",
     "make_block_table",
+    "tree_mask_rows",
     "tree_mask_words",
 ]

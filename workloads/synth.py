@@ -167,6 +167,23 @@ def layout_paged(inp: Inputs, table: np.ndarray, num_blocks: int, block_size: in
     return pk, pv
 
 
+def tree_mask_rows(parents) -> np.ndarray:
+    """The mask rows of a draft tree as the attention call takes them for any
+    T: uint32 [T, (T + 31) // 32], bit u of row t (word u // 32, bit u % 32)
+    set when new token u is t itself or one of its ancestors."""
+    T = len(parents)
+    tw = (T + 31) // 32
+    rows = np.zeros((T, tw), dtype=np.uint32)
+    for t in range(T):
+        u = t
+        while u >= 0:
+            if parents[u] >= u:
+                raise ValueError("a parent must come before its child")
+            rows[t, u // 32] |= np.uint32(1 << (u % 32))
+            u = parents[u]
+    return rows
+
+
 def tree_mask_words(parents) -> np.ndarray:
     """Mask words describing a draft tree among the T new tokens, as the
     caller hands them to the attention call: word t has bit u set when new
