@@ -8,20 +8,21 @@
 // a workgroup hold 32 rows each and compute on the same K/V tiles: the
 // workgroup copies each 32-token tile into LDS together (every wave a
 // quarter of its copy instructions), and a barrier per tile makes all
-// quarters visible and frees the slots of the tile before. One fetch of a
-// K/V row thus serves 128 query rows, where the per-wave form (each wave its
-// own tile for all of the unit's rows) serves at most 64; long blocks re-read
-// the K/V rows once per row block, and with fewer rows per block those
-// re-reads bound the per-wave form on prefill-sized chunks.
+// quarters visible and frees the slot of the tile before. One fetch of a K/V
+// row thus serves 128 query rows.
 //
-// Per tile and wave the arithmetic is that of the per-wave form
-// (v_mfma_f32_16x16x32_{bf16,f16}, transposed score block, p split into a
-// 16-bit high part and remainder, kvc_mfma.h): S^T = K . Q^T over the wave's
-// two 16-row blocks, online softmax in fp32, O^T += V^T . P^T. The query
-// rows live in LDS (each wave copies its own); the K/V tiles come through a
-// ring of `nslots` halves (K and V tiles alternating), all but the tile in
-// use in flight. Every wave computes every live tile of the unit; the key
-// mask is evaluated only on tiles not wholly visible to its rows.
+// Per tile and wave (v_mfma_f32_16x16x32_{bf16,f16}, transposed score block):
+// S^T = K . Q^T over the wave's two 16-row blocks, the query operand held in
+// registers for the whole segment; online softmax in fp32 with the scale
+// folded into the exponent's argument (exp2(s * c - m), c = |scale| log2 e;
+// a negative scale flips the sign bits of the query operand instead, which
+// is exact); p split into a 16-bit high part and the remainder
+// (split_pair_fast); O^T += V^T . P^T. The K/V tiles come through a 64 KB
+// ring of NR slots (a K tile and a V tile each), up to NR - 1 tiles in
+// flight ahead of the one in use; the ring is refilled within a segment
+// only, so each segment (one unit's share of this workgroup's range) starts
+// with its own prologue of copies. The key mask is evaluated only on tiles
+// not wholly visible to a wave's rows.
 #include "kvc.h"
 #include "kvc_device.h"
 #include "kvc_dma.h"
@@ -45,101 +46,125 @@ __device__ __forceinline__ uint32_t tree_word(const uint32_t (&row)[TREE_WORDS],
   return v;
 }
 constexpr int RW = NB * 16;          // query rows per wave
-constexpr int MAX_SLOTS = 8;         // ring halves (waits are counted up to this)
-constexpr int MIN_SLOTS = 4;         // a tile in use and the next one in flight
-constexpr int SLOTS_TWO_PER_CU = 5;  // ring halves when two workgroups share a CU
 constexpr int STATIC_LDS = 256;      // upper bound of the kernel's static LDS
+constexpr int LDS_PER_CU = 160 * 1024;
+constexpr int RING_BYTES = 64 * 1024;  // the K/V ring: 4 slots at H = 128, 8 at H = 64
 
-template <int H>
-constexpr size_t tile_bytes() { return (size_t)TILE * H * 2; }
+// Ring slots: a K tile and a V tile each.
+__host__ __device__ constexpr int ring_slots(int H) { return RING_BYTES / (2 * TILE * H * 2); }
 
-__host__ __device__ constexpr size_t wide_dynamic_lds(int B, int H, int nslots) {
-  return prefix_bytes(B) + (size_t)WIDE_ROWS * H * 2 + (size_t)nslots * TILE * H * 2;
+__host__ __device__ constexpr size_t wide_dynamic_lds(int B) {
+  return prefix_bytes(B) + (size_t)RING_BYTES;
 }
 
-// Wait until the copies of the half issued `later` halves before the newest
-// one have landed (this wave's share: NIW instructions per half).
-template <int NIW>
-__device__ __forceinline__ void wait_halves(int later) {
+// Wait until this wave's copies of the tile that `later` tiles were issued
+// after have landed (NT instructions per tile; later < 8).
+template <int NT>
+__device__ __forceinline__ void wait_tiles(int later) {
   switch (later) {
-    case 1: wait_vm<NIW>(); break;
-    case 2: wait_vm<2 * NIW>(); break;
-    case 3: wait_vm<3 * NIW>(); break;
-    case 4: wait_vm<4 * NIW>(); break;
-    case 5: wait_vm<5 * NIW>(); break;
-    case 6: wait_vm<6 * NIW>(); break;
-    case 7: wait_vm<7 * NIW>(); break;
-    default: wait_vm<0>(); break;  // none later (or more than a ring holds): all
+    case 1: wait_vm<NT>(); break;
+    case 2: wait_vm<2 * NT>(); break;
+    case 3: wait_vm<3 * NT>(); break;
+    case 4: wait_vm<4 * NT>(); break;
+    case 5: wait_vm<5 * NT>(); break;
+    case 6: wait_vm<6 * NT>(); break;
+    default: wait_vm<0>(); break;  // none later: all
   }
 }
 
-// The workgroup's walk over the live tiles of its range, in order: every
-// tile of every step except those holding no key any row of the unit can
-// see (past the sequence's end; with a window, wholly before its first
-// visible key). Live tiles of a step are consecutive and every step holds
-// at least one (its unit's first step holds the first visible key, its last
-// step the last key).
-template <bool MASKED>
-struct TileWalk {
-  StepCursor st;  // as wave 0 sees it: st.tok0 is the step's first token
-  int sub;        // tile within the step
-
-  __device__ __forceinline__ bool live(const AttnArgs& a, int j) const {
-    const int t0 = st.tok0 + j * TILE;
-    return t0 < st.s.seq_len && (!MASKED || t0 + TILE > first_visible(a, st.s.seq_len));
-  }
-  __device__ __forceinline__ int tok0() const { return st.tok0 + sub * TILE; }
-  __device__ __forceinline__ void first_live(const AttnArgs& a) {
-    sub = 0;
-    while (sub < WAVES - 1 && !live(a, sub)) ++sub;
-  }
-  __device__ __forceinline__ void begin(const AttnArgs& a, const int32_t* s_pre, const Partition& p) {
-    st.begin(a, s_pre, p, p.lo, 0);
-    first_live(a);
-  }
-  __device__ __forceinline__ bool step_last(const AttnArgs& a) const {
-    return sub == WAVES - 1 || !live(a, sub + 1);
-  }
-  // the current tile is its segment's last / the range's last
-  __device__ __forceinline__ bool seg_last(const AttnArgs& a) const { return st.x + 1 == st.end && step_last(a); }
-  __device__ __forceinline__ bool range_last(const AttnArgs& a, const Partition& p) const {
-    return st.x + 1 == p.hi && step_last(a);
-  }
-  // to the next live tile (the current one is not the range's last)
-  __device__ __forceinline__ void next(const AttnArgs& a, const int32_t* s_pre, const Partition& p) {
-    if (!step_last(a)) {
-      ++sub;
-      return;
-    }
-    st.advance(a, s_pre, p);
-    first_live(a);
-  }
+// Two probability weights e0, e1 (finite, >= 0) as a packed 16-bit high part
+// and a packed 16-bit remainder, hi + lo = e to about 2^-16 relative: the
+// high part is one packed conversion; each remainder e - hi is one dot
+// product of the packed high part with (-1, 0) or (0, -1) accumulated onto
+// e, exact in fp32 (hi is e rounded to 16 bits, so e - hi is representable);
+// the remainders are packed by one more conversion. The (-1, 0) and (0, -1)
+// pairs come in registers (split_constants): as inline constants of the dot
+// product their 16-bit encoding would be the assembler's to choose.
+struct SplitConsts {
+  uint32_t nx, ny;
 };
+template <bool BF>
+__device__ __forceinline__ SplitConsts split_constants() {
+  // -1 in the low / high half: bf16 0xBF80, f16 0xBC00
+  SplitConsts k{BF ? 0x0000BF80u : 0x0000BC00u, BF ? 0xBF800000u : 0xBC000000u};
+  asm volatile("" : "+v"(k.nx), "+v"(k.ny));
+  return k;
+}
+template <bool BF>
+__device__ __forceinline__ void split_pair_fast(float e0, float e1, const SplitConsts& k, uint32_t& hi,
+                                                uint32_t& lo) {
+  typedef __attribute__((ext_vector_type(2))) float float2_t;
+  if constexpr (BF) {
+    const bf162_t h = __builtin_convertvector((float2_t){e0, e1}, bf162_t);
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf162_t, k.nx), e0, false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf162_t, k.ny), e1, false);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){r0, r1}, bf162_t));
+  } else {
+    const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+    const float r0 = __builtin_amdgcn_fdot2(h, __builtin_bit_cast(half2_t, k.nx), e0, false);
+    const float r1 = __builtin_amdgcn_fdot2(h, __builtin_bit_cast(half2_t, k.ny), e1, false);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+  }
+}
+
+// Four consecutive output elements of one row (idx: the first, a multiple
+// of 4) in the output dtype, one 8- or 16-byte store.
+__device__ __forceinline__ void store_out4(void* out, int64_t idx, int out_dtype, float v0, float v1, float v2,
+                                           float v3) {
+  if (out_dtype == 2) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(v0, v1, v2, v3);
+  } else {
+    uint32_t w0, w1;
+    if (out_dtype == 1) {
+      w0 = f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+      w1 = f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
+    } else {
+      w0 = f32_to_f16_bits(v0) | ((uint32_t)f32_to_f16_bits(v1) << 16);
+      w1 = f32_to_f16_bits(v2) | ((uint32_t)f32_to_f16_bits(v3) << 16);
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = make_uint2(w0, w1);
+  }
+}
+
+// Four consecutive floats of a partial, written through to the memory side
+// (a volatile global store: system-scope coherent, like store_coherent's
+// device-scope store it does not leave the data in this XCD's L2 alone).
+typedef float float4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_coherent4(float* p, float v0, float v1, float v2, float v3) {
+  typedef volatile __attribute__((address_space(1))) float4_t* global_f4_ptr;
+  *(global_f4_ptr)(p) = (float4_t){v0, v1, v2, v3};
+}
 
 }  // namespace
 
 int wide_workgroups_per_cu(int B, int H) {
-  return wide_dynamic_lds(B, H, SLOTS_TWO_PER_CU) + STATIC_LDS <= 80 * 1024 ? 2 : 1;
+  (void)H;
+  return wide_dynamic_lds(B) + STATIC_LDS <= LDS_PER_CU / 2 ? 2 : 1;
 }
 
 template <bool BF, int H, bool PAGED, bool MASKED>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_wide_kernel(AttnArgs a, int nslots) {
+void attn_wide_kernel(AttnArgs a) {
   constexpr int KS = H / 32;     // k-steps of S^T over h
   constexpr int MH = H / 16;     // 16-row h blocks of O^T
   constexpr int ROWB = H * 2;
-  constexpr int NI = TILE * ROWB / 1024;  // copy instructions per tile
+  constexpr int HALFB = TILE * ROWB;      // one K or V tile
+  constexpr int NI = HALFB / 1024;        // copy instructions per K or V tile
   constexpr int NIW = NI / WAVES;         // a wave's share of them
   static_assert(NI % WAVES == 0, "a tile's copies split evenly over the waves");
-  constexpr int TILEB = TILE * ROWB;
-  constexpr int QI = RW * ROWB / 1024;    // copy instructions of a wave's query rows
+  constexpr int SLOTB = 2 * HALFB;        // ring slot: the K tile, then the V tile
+  constexpr int NR = ring_slots(H);
+  constexpr int DEPTH = NR - 1;           // tiles in flight ahead of the one in use
+  static_assert(DEPTH >= 2 && DEPTH <= 7, "waits are counted for these depths");
 
-  // [2B + 1], the unit's query rows (RW per wave), then the ring
+  // [2B + 1], then the ring
   extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];
   __shared__ int32_t s_wave[WAVES], s_flag[2];
-  __shared__ int32_t s_bad[16];  // per segment ordinal mod 16: a bad block entry was met
+  __shared__ int32_t s_bad[4];  // per segment ordinal mod 4: a bad block entry was met
 
-  if (threadIdx.x < 16) s_bad[threadIdx.x] = 0;  // ordered by the barriers below
+  if (threadIdx.x < 4) s_bad[threadIdx.x] = 0;  // ordered by the barriers below
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a, s_pre);
   const int worker = worker_of(a, blockIdx.x);
@@ -151,21 +176,18 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int c = lane & 15;   // column (query row) / A-row (token or h) within a 16 block
   const int g = lane >> 4;   // k-slot group
-  char* qarea = reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B);
-  char* qwave = qarea + wave * RW * ROWB;  // this wave's rows, swizzled as K
-  char* ring = qarea + WIDE_ROWS * ROWB;
+  char* ring = reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B);
   const uint32_t ring_lds = lds_addr(ring);
   const lds_char* ring3 = (const lds_char*)ring;
 
-  // chunk swizzles, as in the per-wave form: 16-byte chunk j of row r at
-  // position j ^ swz(r), so that the A-operand reads are conflict-free
+  // chunk swizzles: 16-byte chunk j of row r at position j ^ swz(r), so that
+  // the A-operand reads are conflict-free
   auto swz_k = [](int r) { return H == 128 ? (r & 15) : ((r >> 1) & 7); };
   auto swz_v = [](int r) { return H == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
   uint32_t lvk[NIW], lvv[NIW];
   tile_lane_offsets<H, NIW>(a, lane, swz_k, lvk, wave * NIW);
   tile_lane_offsets<H, NIW>(a, lane, swz_v, lvv, wave * NIW);
-  // A operand of S^T (K rows 16 mb + c) and B operand (query rows 16 nb + c):
-  // chunk 4 ks + g; swz_k(16 m + c) == swz_k(c)
+  // A operand of S^T (K rows 16 mb + c): chunk 4 ks + g; swz_k(16 m + c) == swz_k(c)
   uint32_t koff[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koff[ks] = c * ROWB + 16 * ((4 * ks + g) ^ swz_k(c));
@@ -178,70 +200,80 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
     for (int mh = 0; mh < MH; ++mh)
       voff[mh] = r * ROWB + 16 * ((2 * mh + (b >> 1)) ^ swz_v(r)) + 8 * (b & 1);
   }
+  // the exponent's scale c > 0; a negative scale negates the query operand.
+  // A scale below the smallest normal float (zero included) is taken as that
+  // value: every s * c then rounds away in exp2(s * c - m) just as s * 0
+  // would, while masked scores (-inf) keep -inf * c = -inf.
+  const float sc = fmaxf(fabsf(a.scale_log2), __FLT_MIN__);
+  const SplitConsts skc = split_constants<BF>();
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-  // ---- copies: halves K(t), V(t) of the live tiles t in walk order
-  TileWalk<MASKED> pc;
-  pc.begin(a, s_pre, part);
-  bool pdone = false;  // every half of the range issued
-  bool pv = false;     // next one is a V half
-  int hp = 0;          // halves issued
-  int pslot = 0;       // slot of the next one
-  auto issue_next = [&]() __attribute__((always_inline)) {
-    const uint32_t dst = ring_lds + pslot * TILEB;
-    bool bad = false;
-    if (!pv) {
-      copy_tile_part<H, PAGED, MASKED, NIW>(a, pc.st.s, pc.st.kb, pc.tok0(), dst, lane, swz_k, lvk,
-                                            wave * NIW, bad);
-    } else {
-      copy_tile_part<H, PAGED, MASKED, NIW>(a, pc.st.s, pc.st.vb, pc.tok0(), dst, lane, swz_v, lvv,
-                                            wave * NIW, bad);
-    }
-    if (PAGED && __ballot(bad) != 0ull && lane == 0) atomicOr(&s_bad[pc.st.ord & 15], 1);
-    if (pv) {
-      if (pc.range_last(a, part)) pdone = true; else pc.next(a, s_pre, part);
-    }
-    pv = !pv;
-    ++hp;
-    pslot = pslot + 1 == nslots ? 0 : pslot + 1;
-  };
-  int hc = 0;     // halves consumed (the K half of the tile in use)
-  int cslot = 0;  // its slot
-  // keep the ring full: every slot but the tile in use (and, before the
-  // barrier that frees them, the previous tile's) holds a half in flight
-  auto fill = [&]() __attribute__((always_inline)) {
-    while (!pdone && hp - hc < nslots) issue_next();
-  };
-  fill();
-
-  TileWalk<MASKED> cs;
-  cs.begin(a, s_pre, part);
   SharedUnits shared;
-  while (true) {
-    const Segment s = cs.st.s;
-    const int ord = cs.st.ord;
+  // Ring slots run on across segments: a segment's prologue fills the slots
+  // after the previous segment's last tile, which a slower wave may still be
+  // reading (a prologue holds at most NR - 1 tiles, so it never reaches
+  // that slot; the first barrier of the segment frees it).
+  int islot = 0;  // slot of the next tile issued
+  int cslot = 0;  // slot of the next tile computed
+  int64_t x = part.lo;
+  for (int ord = 0; x < part.hi; ++ord) {
+    const Segment s = find_segment(a, s_pre, part, x);
+    x += s.t_end - s.t_begin;
+    // live tiles: the segment's tokens up to the sequence's end (and, with a
+    // window, from the tile holding the first visible key); never empty
+    int t_lo = s.t_begin * STEP;
+    if (MASKED) t_lo = max(t_lo, first_visible(a, s.seq_len) & ~(TILE - 1));
+    const int t_hi = min(s.t_end * STEP, s.seq_len);
+    const int nt = __builtin_amdgcn_readfirstlane((t_hi - t_lo + TILE - 1) / TILE);
+    const int64_t hoff = (int64_t)s.k * a.stride_head + (PAGED ? 0 : (int64_t)s.b * a.stride_seq);
+    const char* kb = a.k + hoff;
+    const char* vb = a.v + hoff;
+    int* bad_flag = &s_bad[ord & 3];
+
     const int row0w = s.rb * a.RMAX + wave * RW;  // this wave's first row of the unit
     const int tq_lo = min(row0w, a.R - 1) / a.G;  // its first new token
-    int tq[NB];         // new-token index of this lane's query column
-    uint32_t tw[NB][TREE_WORDS];  // its tree-mask row (T <= KVC_MAX_TREE_T)
+    const int new0 = s.seq_len - a.T;
+    // this wave's query rows as the B operand of S^T: rows 16 nb + c, chunk
+    // 4 ks + g (rows past R repeat row R - 1; their columns are discarded)
+    uint4 qv[NB][KS];
+    int tq[NB];                   // new-token index of this lane's query column
+    uint32_t tw[NB][TREE_WORDS];  // its tree-mask row
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int rr = row0w + nb * 16 + c;
-      tq[nb] = rr < a.R ? rr / a.G : a.T - 1;  // padding column: any valid row, discarded
+      const int rr = min(row0w + nb * 16 + c, a.R - 1);
+      tq[nb] = rr / a.G;
+      const char* qrow = a.q + row_index(a, s.b, s.k, rr) * ROWB;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * (4 * ks + g));
+        v.x ^= qsign;
+        v.y ^= qsign;
+        v.z ^= qsign;
+        v.w ^= qsign;
+        qv[nb][ks] = v;
+      }
       const uint32_t* trow = MASKED && a.tree ? a.tree + ((int64_t)s.b * a.T + tq[nb]) * a.tree_words : nullptr;
 #pragma unroll
       for (int w = 0; w < TREE_WORDS; ++w) tw[nb][w] = trow && w < a.tree_words ? trow[w] : 0u;
     }
-    // this wave's query rows into its LDS rows (rows past R repeat row R - 1;
-    // their columns are discarded); only this wave reads them
-#pragma unroll
-    for (int i = 0; i < QI; ++i) {
-      const int q = i * 64 + lane;  // 16-byte chunk of the wave's rows
-      const int r = q / (ROWB / 16);
-      const int j = (q % (ROWB / 16)) ^ swz_k(r);
-      const int rr = min(row0w + r, a.R - 1);
-      dma16_addr(a.q + row_index(a, s.b, s.k, rr) * ROWB + j * 16, lds_addr(qwave) + i * 1024);
+
+    // tile j of the segment into ring slot `slot`
+    auto issue = [&](int j, int slot) __attribute__((always_inline)) {
+      const int tok = t_lo + j * TILE;
+      const uint32_t dst = ring_lds + slot * SLOTB;
+      bool bad = false;
+      copy_tile_part<H, PAGED, MASKED, NIW>(a, s, kb, tok, dst, lane, swz_k, lvk, wave * NIW, bad);
+      copy_tile_part<H, PAGED, MASKED, NIW>(a, s, vb, tok, dst + HALFB, lane, swz_v, lvv, wave * NIW, bad);
+      if (PAGED && __ballot(bad) != 0ull && lane == 0) atomicOr(bad_flag, 1);
+    };
+    const int pro = min(DEPTH, nt);
+    for (int j = 0; j < pro; ++j) {
+      issue(j, islot);
+      islot = islot + 1 == NR ? 0 : islot + 1;
     }
-    wait_vm<0>();  // the query rows (and every copy issued before them)
+    // the query rows and tree words have landed (the compiler's own wait,
+    // which also covers the copies just issued); later uses wait no more
+    asm volatile("" ::"v"(qv[0][0].x), "v"(qv[NB - 1][KS - 1].w), "v"(tw[0][0]), "v"(tw[NB - 1][TREE_WORDS - 1]));
 
     floatx4 ot[MH][NB];
 #pragma unroll
@@ -254,136 +286,125 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
       m[nb] = NEG_BIG;
       l[nb] = 0.f;
     }
-    const int new0 = s.seq_len - a.T;
 
-    for (;;) {
-      // this wave's quarters of K(t) and V(t) have landed; after the barrier
-      // every wave's have, and every wave is done with the previous tile
-      wait_halves<NIW>(hp - hc - 2);
+    for (int i = 0; i < nt; ++i) {
+      // this wave's copies of tile i have landed; after the barrier every
+      // wave's have, and every wave is done with tile i - 1, whose slot the
+      // next issue refills
+      if (i + DEPTH <= nt)
+        wait_vm<(DEPTH - 1) * 2 * NIW>();
+      else
+        wait_tiles<2 * NIW>(nt - i - 1);
       __syncthreads();
-      fill();
-      const int kslot = cslot;
-      const int vslot = cslot + 1 == nslots ? 0 : cslot + 1;
+      if (i + DEPTH < nt) {
+        issue(i + DEPTH, islot);
+        islot = islot + 1 == NR ? 0 : islot + 1;
+      }
+      const int tok0 = t_lo + i * TILE;
 
-      // Every wave computes every tile, masked where needed: a branch around
-      // the products (skipping tiles a wave's rows cannot see) makes the
-      // compiler copy the accumulators in and out of it on every tile.
-      const int tok0 = cs.tok0();
-      {
-        // ---- S^T = K . Q^T
-        const char* kt = ring + kslot * TILEB;
-        uint4 kf[2][KS];
+      // ---- S^T = K . Q^T
+      const char* kt = ring + cslot * SLOTB;
+      uint4 kf[2][KS];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            kf[mb][ks] = *reinterpret_cast<const uint4*>(kt + koff[ks] + mb * 16 * ROWB);
-        floatx4 st[2][NB];
+        for (int ks = 0; ks < KS; ++ks)
+          kf[mb][ks] = *reinterpret_cast<const uint4*>(kt + koff[ks] + mb * 16 * ROWB);
+      floatx4 st[2][NB];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; ++nb) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-              const uint4 qv = *reinterpret_cast<const uint4*>(qwave + nb * 16 * ROWB + koff[ks]);
-              acc = mfma16<BF>(kf[mb][ks], qv, acc);
-            }
-            st[mb][nb] = acc;
-          }
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16<BF>(kf[mb][ks], qv[nb][ks], acc);
+          st[mb][nb] = acc;
+        }
 
-        // ---- scale, mask, online softmax (one query row per lane column);
-        // tiles wholly visible to every row of this wave skip the test
-        const bool edge = tok0 + TILE > (MASKED && a.tree ? new0 : new0 + 1 + tq_lo) ||
-                          (MASKED && a.window > 0 && tok0 < s.seq_len - a.window);
-        float p[NB][2][4], mt[NB];
+      // ---- mask (tiles not wholly visible to every row of this wave),
+      // tile max, online softmax (one query row per lane column)
+      const bool edge = tok0 + TILE > (MASKED && a.tree ? new0 : new0 + 1 + tq_lo) ||
+                        (MASKED && a.window > 0 && tok0 < s.seq_len - a.window);
+      if (edge) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[nb][mb][i] = st[mb][nb][i] * a.scale_log2;
-        if (edge) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int tok = tok0 + mb * 16 + 4 * g + i;
-                if (!(MASKED ? key_visible(a, tok, new0, tq[nb], tree_word(tw[nb], tok - new0))
-                             : tok <= new0 + tq[nb]))
-                  p[nb][mb][i] = -__builtin_inff();
-              }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          mt[nb] = fmaxf(fmaxf(fmaxf(p[nb][0][0], p[nb][0][1]), fmaxf(p[nb][0][2], p[nb][0][3])),
-                         fmaxf(fmaxf(p[nb][1][0], p[nb][1][1]), fmaxf(p[nb][1][2], p[nb][1][3])));
-        }
-        bool grow = false;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          mt[nb] = max_cols4(mt[nb]);
-          grow |= mt[nb] > m[nb] + RESCALE_MARGIN;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const float mn = mt[nb] > m[nb] + RESCALE_MARGIN ? mt[nb] : m[nb];
-            const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);  // 1 where unchanged
-            l[nb] *= alpha;
-#pragma unroll
-            for (int mh = 0; mh < MH; ++mh) ot[mh][nb] *= alpha;
-            m[nb] = mn;
-          }
-        }
-        uint4 phi[NB], plo[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          uint32_t hw[4], lw[4];
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-              const float e0 = __builtin_amdgcn_exp2f(p[nb][mb][i] - m[nb]);
-              const float e1 = __builtin_amdgcn_exp2f(p[nb][mb][i + 1] - m[nb]);
-              l[nb] += e0 + e1;
-              split_pair<BF>(e0, e1, hw[mb * 2 + i / 2], lw[mb * 2 + i / 2]);
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int tok = tok0 + mb * 16 + 4 * g + i4;
+              if (!(MASKED ? key_visible(a, tok, new0, tq[nb], tree_word(tw[nb], tok - new0))
+                           : tok <= new0 + tq[nb]))
+                st[mb][nb][i4] = -__builtin_inff();
             }
-          phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        }
-
-        // ---- O^T += V^T . P^T
-        const lds_char* vt_base = ring3 + vslot * TILEB;
+      }
+      float mt[NB];
 #pragma unroll
-        for (int mh = 0; mh < MH; ++mh) {
-          const uint2 lo4 = read_tr16(vt_base + voff[mh]);
-          const uint2 hi4 = read_tr16(vt_base + voff[mh] + 16 * ROWB);
-          const uint4 v = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+      for (int nb = 0; nb < NB; ++nb) {
+        const float mr = fmaxf(fmaxf(fmaxf(st[0][nb][0], st[0][nb][1]), fmaxf(st[0][nb][2], st[0][nb][3])),
+                               fmaxf(fmaxf(st[1][nb][0], st[1][nb][1]), fmaxf(st[1][nb][2], st[1][nb][3])));
+        // (a row with no visible key in the tile: -inf, which does not
+        // raise the running max)
+        mt[nb] = max_cols4(mr) * sc;
+      }
+      bool grow = false;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            ot[mh][nb] = mfma16<BF>(v, phi[nb], ot[mh][nb]);
-            ot[mh][nb] = mfma16<BF>(v, plo[nb], ot[mh][nb]);
-          }
+      for (int nb = 0; nb < NB; ++nb) grow |= mt[nb] > m[nb] + RESCALE_MARGIN;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const float mn = mt[nb] > m[nb] + RESCALE_MARGIN ? mt[nb] : m[nb];
+          const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);  // 1 where unchanged
+          l[nb] *= alpha;
+#pragma unroll
+          for (int mh = 0; mh < MH; ++mh) ot[mh][nb] *= alpha;
+          m[nb] = mn;
         }
       }
-      hc += 2;  // both halves are released at the next barrier
-      cslot = vslot + 1 == nslots ? 0 : vslot + 1;
-      if (cs.seg_last(a)) break;
-      cs.next(a, s_pre, part);
+      uint4 phi[NB], plo[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; i4 += 2) {
+            // a masked score (-inf) gives exp2(-inf) = 0
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4], sc, -m[nb]));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4 + 1], sc, -m[nb]));
+            l[nb] += e0 + e1;
+            split_pair_fast<BF>(e0, e1, skc, hw[mb * 2 + i4 / 2], lw[mb * 2 + i4 / 2]);
+          }
+        phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
+
+      // ---- O^T += V^T . P^T
+      const lds_char* vt_base = ring3 + cslot * SLOTB + HALFB;
+#pragma unroll
+      for (int mh = 0; mh < MH; ++mh) {
+        const uint2 lo4 = read_tr16(vt_base + voff[mh]);
+        const uint2 hi4 = read_tr16(vt_base + voff[mh] + 16 * ROWB);
+        const uint4 v = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          ot[mh][nb] = mfma16<BF>(v, phi[nb], ot[mh][nb]);
+          ot[mh][nb] = mfma16<BF>(v, plo[nb], ot[mh][nb]);
+        }
+      }
+      cslot = cslot + 1 == NR ? 0 : cslot + 1;
     }
 
     // ---- per-column totals of l (lanes of one column hold different tokens)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) l[nb] = sum_cols4(l[nb]);
     // Every wave issued this segment's copies before the barrier of its last
-    // tile, so the flag is final; the entry 8 ordinals ahead (never touched
-    // by copies in flight, which run at most MAX_SLOTS / 2 tiles ahead) is
-    // cleared for reuse.
-    const bool bad = PAGED && s_bad[ord & 15] != 0;
-    if (PAGED && wave == 0 && lane == 0) s_bad[(ord + 8) & 15] = 0;
+    // tile, so the flag is final. The flag two segments ahead is cleared
+    // here: its last readers (two segments back) passed this segment's first
+    // barrier before it, and its first writers come after the next
+    // segment's first barrier, which wave 0 reaches only after clearing it.
+    const bool bad = PAGED && *bad_flag != 0;
+    if (PAGED && wave == 0 && lane == 0) s_bad[(ord + 2) & 3] = 0;
 
     // ---- this wave's rows: the output, or a partial counted at the range's end
     const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);  // valid rows of the unit
@@ -393,12 +414,13 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
       for (int nb = 0; nb < NB; ++nb) {
         const int lr = wave * RW + nb * 16 + c;
         if (lr < rows) {
+          const int64_t ri = row_index(a, s.b, s.k, s.rb * a.RMAX + lr);
+          const float inv = bad ? qnan : 1.0f / l[nb];
 #pragma unroll
           for (int mh = 0; mh < MH; ++mh)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              write_final(a, s.b, s.k, s.rb * a.RMAX + lr, H, mh * 16 + 4 * g + i,
-                          bad ? qnan : ot[mh][nb][i], bad ? qnan : m[nb], bad ? qnan : l[nb]);
+            store_out4(a.out, ri * H + mh * 16 + 4 * g, a.out_dtype, ot[mh][nb][0] * inv, ot[mh][nb][1] * inv,
+                       ot[mh][nb][2] * inv, ot[mh][nb][3] * inv);
+          if (g == 0 && a.lse) a.lse[ri] = bad ? qnan : (m[nb] + __log2f(l[nb])) * LN2;
         }
       }
     } else {
@@ -410,10 +432,11 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
         const int lr = wave * RW + nb * 16 + c;
         if (lr < rows) {
 #pragma unroll
-          for (int mh = 0; mh < MH; ++mh)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              store_coherent(po + lr * H + mh * 16 + 4 * g + i, bad ? qnan : ot[mh][nb][i]);
+          for (int mh = 0; mh < MH; ++mh) {
+            const floatx4 o = ot[mh][nb];
+            store_coherent4(po + lr * H + mh * 16 + 4 * g, bad ? qnan : o[0], bad ? qnan : o[1],
+                            bad ? qnan : o[2], bad ? qnan : o[3]);
+          }
           if (g == 0) {
             store_coherent(pml + lr * 2 + 0, bad ? qnan : m[nb]);
             store_coherent(pml + lr * 2 + 1, bad ? qnan : l[nb]);
@@ -422,20 +445,17 @@ void attn_wide_kernel(AttnArgs a, int nslots) {
       }
       shared.add(s);
     }
-    if (cs.range_last(a, part)) break;
-    cs.next(a, s_pre, part);
   }
-  // every copy has landed and been read: the query rows and the ring are free
+  // every copy has landed and been read: the ring is free
   __syncthreads();
-  count_and_merge<H, WIDE_ROWS * H / THREADS>(a, shared, s_flag, reinterpret_cast<float*>(qarea),
-                                              (int)((WIDE_ROWS * ROWB + nslots * TILEB) / 4));
+  count_and_merge<H, WIDE_ROWS * H / THREADS>(a, shared, s_flag, reinterpret_cast<float*>(ring),
+                                              RING_BYTES / 4);
 }
 
 // ---------------------------------------------------------------- launch
 
 template <bool BF, int H, bool PAGED, bool MASKED>
 static hipError_t launch_wide_t(const AttnArgs& a, hipStream_t stream) {
-  constexpr int LDS_PER_CU = 160 * 1024;
   const auto kern = attn_wide_kernel<BF, H, PAGED, MASKED>;
   static size_t static_lds = 0;
   static const hipError_t attr = [&] {
@@ -448,17 +468,9 @@ static hipError_t launch_wide_t(const AttnArgs& a, hipStream_t stream) {
   }();
   if (attr != hipSuccess) return attr;
   if (a.RMAX != WIDE_ROWS || static_lds > (size_t)STATIC_LDS) return hipErrorInvalidConfiguration;
-  // two workgroups per CU with SLOTS_TWO_PER_CU halves where they fit, else
-  // one with as many halves as its LDS holds
-  int nslots = SLOTS_TWO_PER_CU;
-  if (wide_workgroups_per_cu(a.B, H) == 1) {
-    const size_t fixed = wide_dynamic_lds(a.B, H, 0) + static_lds;
-    nslots = fixed < (size_t)LDS_PER_CU ? (int)((LDS_PER_CU - fixed) / tile_bytes<H>()) : 0;
-    if (nslots > MAX_SLOTS) nslots = MAX_SLOTS;
-    if (nslots < MIN_SLOTS) return hipErrorInvalidConfiguration;
-  }
-  const size_t shmem = wide_dynamic_lds(a.B, H, nslots);
-  hipLaunchKernelGGL(kern, dim3(a.W), dim3(THREADS), shmem, stream, a, nslots);
+  const size_t shmem = wide_dynamic_lds(a.B);
+  if (shmem + static_lds > (size_t)LDS_PER_CU) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3(a.W), dim3(THREADS), shmem, stream, a);
   return hipGetLastError();
 }
 
