@@ -16,9 +16,10 @@
 // registers for the whole segment; online softmax in fp32 with the scale
 // folded into the exponent's argument (exp2(s * c - m), c = |scale| log2 e;
 // a negative scale flips the sign bits of the query operand instead, which
-// is exact); p split into a 16-bit high part and the remainder
-// (split_pair_fast); O^T += V^T . P^T. The K/V tiles come through a 64 KB
-// ring of NR slots (a K tile and a V tile each), up to NR - 1 tiles in
+// is exact), the reference m raised only when the weights show it is needed
+// (no per-tile maximum otherwise); p split into a 16-bit high part and the
+// remainder (split_pair_fast); O^T += V^T . P^T. The K/V tiles come through
+// a 64 KB ring of NR slots (a K tile and a V tile each), up to NR - 1 tiles in
 // flight ahead of the one in use; the ring is refilled within a segment
 // only, so each segment (one unit's share of this workgroup's range) starts
 // with its own prologue of copies. The key mask is evaluated only on tiles
@@ -46,6 +47,9 @@ __device__ __forceinline__ uint32_t tree_word(const uint32_t (&row)[TREE_WORDS],
   return v;
 }
 constexpr int RW = NB * 16;          // query rows per wave
+// A lane's sum of its 8 weights of a row in one tile that leaves every
+// weight within the accumulators' range without a new reference.
+constexpr float WEIGHT_BOUND = 256.0f;
 constexpr int STATIC_LDS = 256;      // upper bound of the kernel's static LDS
 constexpr int LDS_PER_CU = 160 * 1024;
 constexpr int RING_BYTES = 64 * 1024;  // the K/V ring: 4 slots at H = 128, 8 at H = 64
@@ -302,14 +306,28 @@ void attn_wide_kernel(AttnArgs a) {
       }
       const int tok0 = t_lo + i * TILE;
 
-      // ---- S^T = K . Q^T
+      // ---- the tile's operands from LDS, K for S^T and V^T for O^T, all
+      // read up front so that their latency overlaps the first products
+      // (the scheduling barrier keeps the compiler from moving the reads
+      // down to their uses)
       const char* kt = ring + cslot * SLOTB;
+      const lds_char* vt_base = ring3 + cslot * SLOTB + HALFB;
       uint4 kf[2][KS];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           kf[mb][ks] = *reinterpret_cast<const uint4*>(kt + koff[ks] + mb * 16 * ROWB);
+      uint4 vf[MH];
+#pragma unroll
+      for (int mh = 0; mh < MH; ++mh) {
+        const uint2 lo4 = read_tr16(vt_base + voff[mh]);
+        const uint2 hi4 = read_tr16(vt_base + voff[mh] + 16 * ROWB);
+        vf[mh] = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- S^T = K . Q^T
       floatx4 st[2][NB];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -321,8 +339,7 @@ void attn_wide_kernel(AttnArgs a) {
           st[mb][nb] = acc;
         }
 
-      // ---- mask (tiles not wholly visible to every row of this wave),
-      // tile max, online softmax (one query row per lane column)
+      // ---- mask (tiles not wholly visible to every row of this wave)
       const bool edge = tok0 + TILE > (MASKED && a.tree ? new0 : new0 + 1 + tq_lo) ||
                         (MASKED && a.window > 0 && tok0 < s.seq_len - a.window);
       if (edge) {
@@ -338,58 +355,71 @@ void attn_wide_kernel(AttnArgs a) {
                 st[mb][nb][i4] = -__builtin_inff();
             }
       }
-      float mt[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float mr = fmaxf(fmaxf(fmaxf(st[0][nb][0], st[0][nb][1]), fmaxf(st[0][nb][2], st[0][nb][3])),
-                               fmaxf(fmaxf(st[1][nb][0], st[1][nb][1]), fmaxf(st[1][nb][2], st[1][nb][3])));
-        // (a row with no visible key in the tile: -inf, which does not
-        // raise the running max)
-        mt[nb] = max_cols4(mr) * sc;
-      }
-      bool grow = false;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) grow |= mt[nb] > m[nb] + RESCALE_MARGIN;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+
+      // ---- online softmax (one query row per lane column). The weights
+      // 2^(s c - m) are taken against the current reference m first; a
+      // lane's sum of its 8 weights of a row bounds each of them, so while
+      // every such sum is at most 2^8 no weight exceeds 2^8 (the
+      // accumulators' range, as with a lazily raised maximum) and no
+      // maximum is needed. Otherwise (a row's first visible keys, or a key
+      // far above the reference) the reference is raised to the tile's
+      // maximum where that is larger, and the weights are taken again.
+      uint4 phi[NB], plo[NB];
+      float tsum[NB];
+      auto weights = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const float mn = mt[nb] > m[nb] + RESCALE_MARGIN ? mt[nb] : m[nb];
+          uint32_t hw[4], lw[4];
+          float ps[4];
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; i4 += 2) {
+              // a masked score (-inf) gives exp2(-inf) = 0 (c > 0)
+              const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4], sc, -m[nb]));
+              const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4 + 1], sc, -m[nb]));
+              ps[mb * 2 + i4 / 2] = e0 + e1;
+              split_pair_fast<BF>(e0, e1, skc, hw[mb * 2 + i4 / 2], lw[mb * 2 + i4 / 2]);
+            }
+          tsum[nb] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+          phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+      };
+      weights();
+      bool over = false;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) over |= !(tsum[nb] <= WEIGHT_BOUND);  // (NaN: over)
+      if (__builtin_amdgcn_ballot_w64(over) != 0ull) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float p8[8];
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) p8[mb * 4 + i4] = st[mb][nb][i4] * sc;
+          const float mr = fmaxf(fmaxf(fmaxf(p8[0], p8[1]), fmaxf(p8[2], p8[3])),
+                                 fmaxf(fmaxf(p8[4], p8[5]), fmaxf(p8[6], p8[7])));
+          // (-inf for a row with no visible key in the tile: unchanged)
+          const float mn = fmaxf(m[nb], max_cols4(mr));
           const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);  // 1 where unchanged
           l[nb] *= alpha;
 #pragma unroll
           for (int mh = 0; mh < MH; ++mh) ot[mh][nb] *= alpha;
           m[nb] = mn;
         }
+        weights();
       }
-      uint4 phi[NB], plo[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i4 = 0; i4 < 4; i4 += 2) {
-            // a masked score (-inf) gives exp2(-inf) = 0
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4], sc, -m[nb]));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4 + 1], sc, -m[nb]));
-            l[nb] += e0 + e1;
-            split_pair_fast<BF>(e0, e1, skc, hw[mb * 2 + i4 / 2], lw[mb * 2 + i4 / 2]);
-          }
-        phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      }
+      for (int nb = 0; nb < NB; ++nb) l[nb] += tsum[nb];
 
       // ---- O^T += V^T . P^T
-      const lds_char* vt_base = ring3 + cslot * SLOTB + HALFB;
 #pragma unroll
       for (int mh = 0; mh < MH; ++mh) {
-        const uint2 lo4 = read_tr16(vt_base + voff[mh]);
-        const uint2 hi4 = read_tr16(vt_base + voff[mh] + 16 * ROWB);
-        const uint4 v = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          ot[mh][nb] = mfma16<BF>(v, phi[nb], ot[mh][nb]);
-          ot[mh][nb] = mfma16<BF>(v, plo[nb], ot[mh][nb]);
+          ot[mh][nb] = mfma16<BF>(vf[mh], phi[nb], ot[mh][nb]);
+          ot[mh][nb] = mfma16<BF>(vf[mh], plo[nb], ot[mh][nb]);
         }
       }
       cslot = cslot + 1 == NR ? 0 : cslot + 1;
