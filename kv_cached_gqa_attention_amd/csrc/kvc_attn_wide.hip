@@ -113,34 +113,6 @@ __device__ __forceinline__ void split_pair_fast(float e0, float e1, const SplitC
   }
 }
 
-// Four consecutive output elements of one row (idx: the first, a multiple
-// of 4) in the output dtype, one 8- or 16-byte store.
-__device__ __forceinline__ void store_out4(void* out, int64_t idx, int out_dtype, float v0, float v1, float v2,
-                                           float v3) {
-  if (out_dtype == 2) {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(v0, v1, v2, v3);
-  } else {
-    uint32_t w0, w1;
-    if (out_dtype == 1) {
-      w0 = f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
-      w1 = f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
-    } else {
-      w0 = f32_to_f16_bits(v0) | ((uint32_t)f32_to_f16_bits(v1) << 16);
-      w1 = f32_to_f16_bits(v2) | ((uint32_t)f32_to_f16_bits(v3) << 16);
-    }
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = make_uint2(w0, w1);
-  }
-}
-
-// Four consecutive floats of a partial, written through to the memory side
-// (a volatile global store: system-scope coherent, like store_coherent's
-// device-scope store it does not leave the data in this XCD's L2 alone).
-typedef float float4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void store_coherent4(float* p, float v0, float v1, float v2, float v3) {
-  typedef volatile __attribute__((address_space(1))) float4_t* global_f4_ptr;
-  *(global_f4_ptr)(p) = (float4_t){v0, v1, v2, v3};
-}
-
 }  // namespace
 
 int wide_workgroups_per_cu(int B, int H) {

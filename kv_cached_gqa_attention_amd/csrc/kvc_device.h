@@ -64,7 +64,9 @@ struct AttnArgs {
   int32_t RMAX;  // rows per row block (the last block may be partial)
   int32_t out_dtype;  // 0 f16, 1 bf16, 2 f32
   int32_t W;          // workers sharing the tiles (waves or workgroups, per kernel)
-  int32_t fast_workers;  // the first fast_workers get the larger share (0: equal shares)
+  int32_t fast_workers;  // workers with the larger share (0: equal shares; see Partition)
+  int32_t share_fast;    // the larger and the smaller share's weights
+  int32_t share_slow;
   int32_t xcds;       // > 0: workers numbered XCD by XCD (worker_of); 0: worker = workgroup
   float scale_log2;   // scale * log2(e)
   float* part_o;      // [W + units, RMAX, H], slot = worker + unit
@@ -137,6 +139,25 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, int out_dtype,
   }
 }
 
+// Four consecutive output elements of one row (idx: the first, a multiple
+// of 4) in the output dtype, one 8- or 16-byte store.
+__device__ __forceinline__ void store_out4(void* out, int64_t idx, int out_dtype, float v0, float v1, float v2,
+                                           float v3) {
+  if (out_dtype == 2) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(v0, v1, v2, v3);
+  } else {
+    uint32_t w0, w1;
+    if (out_dtype == 1) {
+      w0 = f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+      w1 = f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
+    } else {
+      w0 = f32_to_f16_bits(v0) | ((uint32_t)f32_to_f16_bits(v1) << 16);
+      w1 = f32_to_f16_bits(v2) | ((uint32_t)f32_to_f16_bits(v3) << 16);
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = make_uint2(w0, w1);
+  }
+}
+
 __device__ __forceinline__ uint4 load16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -148,6 +169,22 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 }
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Sixteen / eight bytes written through to, or read from, the memory side:
+// volatile global accesses, coherent at system scope (no stale or dirty copy
+// in this XCD's L2 is used).
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef volatile __attribute__((address_space(1))) float4_t* coherent_f4_ptr;
+typedef volatile __attribute__((address_space(1))) float2_t* coherent_f2_ptr;
+__device__ __forceinline__ void store_coherent4(float* p, float v0, float v1, float v2, float v3) {
+  *(coherent_f4_ptr)(p) = (float4_t){v0, v1, v2, v3};
+}
+__device__ __forceinline__ float4_t load_coherent4(const float* p) {
+  return *(coherent_f4_ptr)(const_cast<float*>(p));
+}
+__device__ __forceinline__ float2_t load_coherent2(const float* p) {
+  return *(coherent_f2_ptr)(const_cast<float*>(p));
 }
 // Wait until this wave's outstanding vector memory operations (stores
 // included) are acknowledged: s_waitcnt vmcnt(0), leaving the LDS and export
@@ -334,34 +371,46 @@ struct Segment {
   int first_wg;   // first worker sharing the unit
 };
 
-// Workers' shares of the steps: equal, or (fast > 0) weighted FAST_SHARE :
-// SLOW_SHARE between the first `fast` workers and the rest. With two
-// workgroups per CU the hardware places workgroup i and i + (number of CUs)
-// on one CU, and the older of the two is served first (about 25% faster);
-// weighting the shares lets both finish together.
-constexpr int FAST_SHARE = 5, SLOW_SHARE = 4;
-
+// Workers' shares of the steps: equal, or (fast > 0) weighted wf : ws
+// between the older and the younger workgroup of each CU. With two
+// workgroups per CU (a full round of 2 x CUs) the first `fast` = CUs
+// workgroups are each the older of a CU's pair, and the older one is served
+// first (about 25% faster on the decode kernels, about 20% on the long-block
+// kernel); weighting the shares lets both finish together. In launch order
+// (per = 0) the fast workers are workers [0, fast); numbered XCD by XCD
+// (worker_of, per = W / xcds workers per XCD) they are the first half of
+// each XCD's block.
 struct Partition {
   int64_t total;  // steps over all units
   int w_eff;      // workers with work: min(W, total); each then has >= 1 step
   int64_t lo, hi; // this worker's flat step range
   int krb;        // K * RB
   int fast;       // workers with the larger share (0: equal shares)
+  int per;        // > 0: fast workers are the first per / 2 of each block of per
+  int wf, ws;     // share weights
   int64_t wt;     // sum of the shares (w_eff when equal)
 
   __device__ int64_t share_prefix(int w) const {  // shares of workers [0, w)
     if (!fast) return w;
-    return w <= fast ? (int64_t)FAST_SHARE * w
-                     : (int64_t)FAST_SHARE * fast + (int64_t)SLOW_SHARE * (w - fast);
+    if (per) {
+      const int h = per >> 1, r = w % per;
+      return (int64_t)(w / per) * h * (wf + ws) + (int64_t)min(r, h) * wf + (int64_t)max(r - h, 0) * ws;
+    }
+    return w <= fast ? (int64_t)wf * w : (int64_t)wf * fast + (int64_t)ws * (w - fast);
   }
   // Worker w's range is [total * P(w) / wt, total * P(w + 1) / wt), P the
   // share prefix; the owner of step x is the largest w with P(w) <= u.
   __device__ int owner(int64_t x) const {  // worker whose range holds step x
     const int64_t u = ((x + 1) * wt - 1) / total;
     if (!fast) return (int)u;
-    const int64_t w = u < (int64_t)FAST_SHARE * fast
-                          ? u / FAST_SHARE
-                          : fast + (u - (int64_t)FAST_SHARE * fast) / SLOW_SHARE;
+    int64_t w;
+    if (per) {
+      const int h = per >> 1;
+      const int64_t bw = (int64_t)h * (wf + ws), blk = u / bw, rem = u - blk * bw;
+      w = blk * per + (rem < (int64_t)h * wf ? rem / wf : h + (rem - (int64_t)h * wf) / ws);
+    } else {
+      w = u < (int64_t)wf * fast ? u / wf : fast + (u - (int64_t)wf * fast) / ws;
+    }
     return (int)(w < w_eff - 1 ? w : w_eff - 1);
   }
 };
@@ -384,9 +433,19 @@ __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int
   p.total = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[a.B]) * p.krb;
   p.w_eff = (int)(p.total < (int64_t)a.W ? p.total : (int64_t)a.W);
   // weighted only with at least two steps per worker, so every share keeps
-  // at least one step (4 / 5 of 2 rounds down to 1)
+  // at least one step (ws / wf of 2 rounds down to 1); numbered XCD by XCD,
+  // only with every worker busy (the block structure)
   p.fast = a.fast_workers > 0 && a.fast_workers < p.w_eff && p.total >= 2 * (int64_t)p.w_eff
                ? a.fast_workers : 0;
+  p.per = 0;
+  if (p.fast && a.xcds > 0) {
+    if (p.w_eff == a.W && a.W == 2 * a.fast_workers && a.fast_workers % a.xcds == 0)
+      p.per = a.W / a.xcds;
+    else
+      p.fast = 0;
+  }
+  p.wf = a.share_fast;
+  p.ws = a.share_slow;
   p.wt = p.share_prefix(p.w_eff);
   if (w < p.w_eff) {
     p.lo = p.total * p.share_prefix(w) / p.wt;
@@ -654,6 +713,85 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, const Segment&
   constexpr int PJ = 32 / EP > 16 ? 16 : 32 / EP;
   const int n = s.n_parts;
   auto slot_of = [&](int j) { return (int64_t)s.first_wg + j + s.unit; };
+  if constexpr (EPT % 4 == 0) {
+    // Four consecutive elements of a row per thread and load (16-byte
+    // loads): passes of up to 8 such chunks, each loading PJ partials'
+    // chunks at once (PJ * EP <= 16 chunks); the first pass's loads are
+    // issued together with the statistics of all partials. Same summation
+    // order as the element-wise form below.
+    if (n * rows * 2 + 2 * rows <= cap && rows * H <= EPT * THREADS) {
+      constexpr int E4 = EPT / 4;
+      constexpr int EP = E4 < 8 ? E4 : 8;
+      constexpr int PJ = 16 / EP > 16 ? 16 : 16 / EP;
+      float* sw = scratch;                // [n][rows]: m, then the weight 2^(m - M)
+      float* sl = scratch + n * rows;     // [n][rows]: l
+      float* sM = scratch + 2 * n * rows; // [rows]: M
+      float* sL = sM + rows;              // [rows]: L
+      const int q_max = rows * H / 4 - 1;
+      auto chunk = [&](int p0, int u) { return min((int)threadIdx.x + (p0 + u) * THREADS, q_max); };
+      float4_t ov[PJ][EP];
+      auto load_o = [&](int p0, int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < PJ; ++jj) {
+          const float* po = a.part_o + slot_of(min(j0 + jj, n - 1)) * a.RMAX * H;
+#pragma unroll
+          for (int u = 0; u < EP; ++u) ov[jj][u] = load_coherent4(po + 4 * chunk(p0, u));
+        }
+      };
+      load_o(0, 0);
+      for (int e = threadIdx.x; e < n * rows; e += THREADS) {
+        const int j = e / rows, r = e - (e / rows) * rows;
+        const float2_t ml = load_coherent2(a.part_ml + slot_of(j) * a.RMAX * 2 + r * 2);
+        sw[e] = ml.x;
+        sl[e] = ml.y;
+      }
+      __syncthreads();
+      for (int r = threadIdx.x; r < rows; r += THREADS) {
+        float M = NEG_BIG;
+        for (int j = 0; j < n; ++j) M = fmaxf(M, sw[j * rows + r]);
+        float L = 0.f;
+        for (int j = 0; j < n; ++j) {
+          const float w = __builtin_amdgcn_exp2f(sw[j * rows + r] - M);
+          sw[j * rows + r] = w;
+          L += w * sl[j * rows + r];
+        }
+        sM[r] = M;
+        sL[r] = L;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p0 = 0; p0 < E4; p0 += EP) {
+        float4_t O[EP];
+#pragma unroll
+        for (int u = 0; u < EP; ++u) O[u] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int j0 = 0; j0 < n; j0 += PJ) {
+          if (p0 > 0 || j0 > 0) load_o(p0, j0);
+#pragma unroll
+          for (int jj = 0; jj < PJ; ++jj) {
+            if (j0 + jj < n) {
+#pragma unroll
+              for (int u = 0; u < EP; ++u) O[u] += sw[(j0 + jj) * rows + 4 * chunk(p0, u) / H] * ov[jj][u];
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < EP; ++u) {
+          const int q = threadIdx.x + (p0 + u) * THREADS;
+          if (p0 + u < E4 && q <= q_max) {
+            const int r = 4 * q / H, h = 4 * q - (4 * q / H) * H;
+            const int64_t ri = row_index(a, s.b, s.k, row0 + r);
+            const float L = sL[r];
+            store_out4(a.out, ri * H + h, a.out_dtype, O[u].x / L, O[u].y / L, O[u].z / L, O[u].w / L);
+            if (h == 0 && a.lse) a.lse[ri] = (sM[r] + __log2f(L)) * LN2;
+          }
+        }
+      }
+      __syncthreads();  // the scratch may be reused
+      if (threadIdx.x == 0)
+        __hip_atomic_store(&a.counters[s.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
   if (n * rows * 2 + 2 * rows <= cap && rows * H <= EPT * THREADS) {
     float* sw = scratch;                // [n][rows]: m, then the weight 2^(m - M)
     float* sl = scratch + n * rows;     // [n][rows]: l
