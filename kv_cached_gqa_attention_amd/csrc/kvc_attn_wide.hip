@@ -436,12 +436,11 @@ void attn_wide_kernel(AttnArgs a) {
 #pragma unroll
           for (int mh = 0; mh < MH; ++mh) {
             const floatx4 o = ot[mh][nb];
-            store_coherent4(po + lr * H + mh * 16 + 4 * g, bad ? qnan : o[0], bad ? qnan : o[1],
-                            bad ? qnan : o[2], bad ? qnan : o[3]);
+            store_coherent2(po + lr * H + mh * 16 + 4 * g, bad ? qnan : o[0], bad ? qnan : o[1]);
+            store_coherent2(po + lr * H + mh * 16 + 4 * g + 2, bad ? qnan : o[2], bad ? qnan : o[3]);
           }
           if (g == 0) {
-            store_coherent(pml + lr * 2 + 0, bad ? qnan : m[nb]);
-            store_coherent(pml + lr * 2 + 1, bad ? qnan : l[nb]);
+            store_coherent2(pml + lr * 2, bad ? qnan : m[nb], bad ? qnan : l[nb]);
           }
         }
       }

@@ -139,6 +139,19 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, int out_dtype,
   }
 }
 
+// Two consecutive output elements of one row (idx even) in the output
+// dtype, one 4- or 8-byte store.
+__device__ __forceinline__ void store_out2(void* out, int64_t idx, int out_dtype, float v0, float v1) {
+  if (out_dtype == 2) {
+    *reinterpret_cast<float2*>(static_cast<float*>(out) + idx) = make_float2(v0, v1);
+  } else if (out_dtype == 1) {
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + idx) =
+        f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+  } else {
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + idx) =
+        f32_to_f16_bits(v0) | ((uint32_t)f32_to_f16_bits(v1) << 16);
+  }
+}
 // Four consecutive output elements of one row (idx: the first, a multiple
 // of 4) in the output dtype, one 8- or 16-byte store.
 __device__ __forceinline__ void store_out4(void* out, int64_t idx, int out_dtype, float v0, float v1, float v2,
@@ -170,21 +183,18 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Sixteen / eight bytes written through to, or read from, the memory side:
-// volatile global accesses, coherent at system scope (no stale or dirty copy
-// in this XCD's L2 is used).
-typedef float float4_t __attribute__((ext_vector_type(4)));
+// Two consecutive floats (8-byte aligned) as one device-coherent 8-byte
+// access: relaxed device-scope atomics, like the scalar pair above (a
+// volatile access would be as coherent, but the compiler waits for each
+// volatile load or store before the next one).
 typedef float float2_t __attribute__((ext_vector_type(2)));
-typedef volatile __attribute__((address_space(1))) float4_t* coherent_f4_ptr;
-typedef volatile __attribute__((address_space(1))) float2_t* coherent_f2_ptr;
-__device__ __forceinline__ void store_coherent4(float* p, float v0, float v1, float v2, float v3) {
-  *(coherent_f4_ptr)(p) = (float4_t){v0, v1, v2, v3};
-}
-__device__ __forceinline__ float4_t load_coherent4(const float* p) {
-  return *(coherent_f4_ptr)(const_cast<float*>(p));
+__device__ __forceinline__ void store_coherent2(float* p, float v0, float v1) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, (float2_t){v0, v1}),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float2_t load_coherent2(const float* p) {
-  return *(coherent_f2_ptr)(const_cast<float*>(p));
+  return __builtin_bit_cast(float2_t, __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 // Wait until this wave's outstanding vector memory operations (stores
 // included) are acknowledged: s_waitcnt vmcnt(0), leaving the LDS and export
@@ -713,29 +723,29 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, const Segment&
   constexpr int PJ = 32 / EP > 16 ? 16 : 32 / EP;
   const int n = s.n_parts;
   auto slot_of = [&](int j) { return (int64_t)s.first_wg + j + s.unit; };
-  if constexpr (EPT % 4 == 0) {
-    // Four consecutive elements of a row per thread and load (16-byte
-    // loads): passes of up to 8 such chunks, each loading PJ partials'
-    // chunks at once (PJ * EP <= 16 chunks); the first pass's loads are
+  if constexpr (EPT % 2 == 0) {
+    // Two consecutive elements of a row per thread and load (8-byte
+    // loads): passes of up to 16 such chunks, each loading PJ partials'
+    // chunks at once (PJ * EP <= 32 chunks); the first pass's loads are
     // issued together with the statistics of all partials. Same summation
     // order as the element-wise form below.
     if (n * rows * 2 + 2 * rows <= cap && rows * H <= EPT * THREADS) {
-      constexpr int E4 = EPT / 4;
-      constexpr int EP = E4 < 8 ? E4 : 8;
-      constexpr int PJ = 16 / EP > 16 ? 16 : 16 / EP;
+      constexpr int E2 = EPT / 2;
+      constexpr int EP = E2 < 16 ? E2 : 16;
+      constexpr int PJ = 32 / EP > 16 ? 16 : 32 / EP;
       float* sw = scratch;                // [n][rows]: m, then the weight 2^(m - M)
       float* sl = scratch + n * rows;     // [n][rows]: l
       float* sM = scratch + 2 * n * rows; // [rows]: M
       float* sL = sM + rows;              // [rows]: L
-      const int q_max = rows * H / 4 - 1;
+      const int q_max = rows * H / 2 - 1;
       auto chunk = [&](int p0, int u) { return min((int)threadIdx.x + (p0 + u) * THREADS, q_max); };
-      float4_t ov[PJ][EP];
+      float2_t ov[PJ][EP];
       auto load_o = [&](int p0, int j0) __attribute__((always_inline)) {
 #pragma unroll
         for (int jj = 0; jj < PJ; ++jj) {
           const float* po = a.part_o + slot_of(min(j0 + jj, n - 1)) * a.RMAX * H;
 #pragma unroll
-          for (int u = 0; u < EP; ++u) ov[jj][u] = load_coherent4(po + 4 * chunk(p0, u));
+          for (int u = 0; u < EP; ++u) ov[jj][u] = load_coherent2(po + 2 * chunk(p0, u));
         }
       };
       load_o(0, 0);
@@ -760,28 +770,28 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, const Segment&
       }
       __syncthreads();
 #pragma unroll
-      for (int p0 = 0; p0 < E4; p0 += EP) {
-        float4_t O[EP];
+      for (int p0 = 0; p0 < E2; p0 += EP) {
+        float2_t O[EP];
 #pragma unroll
-        for (int u = 0; u < EP; ++u) O[u] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < EP; ++u) O[u] = (float2_t){0.f, 0.f};
         for (int j0 = 0; j0 < n; j0 += PJ) {
           if (p0 > 0 || j0 > 0) load_o(p0, j0);
 #pragma unroll
           for (int jj = 0; jj < PJ; ++jj) {
             if (j0 + jj < n) {
 #pragma unroll
-              for (int u = 0; u < EP; ++u) O[u] += sw[(j0 + jj) * rows + 4 * chunk(p0, u) / H] * ov[jj][u];
+              for (int u = 0; u < EP; ++u) O[u] += sw[(j0 + jj) * rows + 2 * chunk(p0, u) / H] * ov[jj][u];
             }
           }
         }
 #pragma unroll
         for (int u = 0; u < EP; ++u) {
           const int q = threadIdx.x + (p0 + u) * THREADS;
-          if (p0 + u < E4 && q <= q_max) {
-            const int r = 4 * q / H, h = 4 * q - (4 * q / H) * H;
+          if (p0 + u < E2 && q <= q_max) {
+            const int r = 2 * q / H, h = 2 * q - (2 * q / H) * H;
             const int64_t ri = row_index(a, s.b, s.k, row0 + r);
             const float L = sL[r];
-            store_out4(a.out, ri * H + h, a.out_dtype, O[u].x / L, O[u].y / L, O[u].z / L, O[u].w / L);
+            store_out2(a.out, ri * H + h, a.out_dtype, O[u].x / L, O[u].y / L);
             if (h == 0 && a.lse) a.lse[ri] = (sM[r] + __log2f(L)) * LN2;
           }
         }
