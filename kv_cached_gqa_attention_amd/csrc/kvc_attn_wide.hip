@@ -139,6 +139,7 @@ void attn_wide_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];
   __shared__ int32_t s_wave[WAVES], s_flag[2];
   __shared__ int32_t s_bad[4];  // per segment ordinal mod 4: a bad block entry was met
+  __shared__ int32_t s_count, s_early;  // a split unit's count; an early part was the last
 
   if (threadIdx.x < 4) s_bad[threadIdx.x] = 0;  // ordered by the barriers below
   build_tile_prefix(a, s_pre, s_wave);
@@ -185,6 +186,8 @@ void attn_wide_kernel(AttnArgs a) {
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   SharedUnits shared;
+  Segment early;             // a unit whose early part was counted last
+  bool early_merge = false;  // (uniform)
   // Ring slots run on across segments: a segment's prologue fills the slots
   // after the previous segment's last tile, which a slower wave may still be
   // reading (a prologue holds at most NR - 1 tiles, so it never reaches
@@ -408,21 +411,74 @@ void attn_wide_kernel(AttnArgs a) {
     const bool bad = PAGED && *bad_flag != 0;
     if (PAGED && wave == 0 && lane == 0) s_bad[(ord + 2) & 3] = 0;
 
-    // ---- this wave's rows: the output, or a partial counted at the range's end
+    // ---- this wave's rows: the output, or a partial. Of a unit split over
+    // several workers, the part in the first segment of a range holds the
+    // unit's later steps and is done early: its partial is counted at once.
+    // The part in the last segment of a range holds the unit's first steps
+    // and is done last: of a unit split in two, when the other part has
+    // been counted, it is merged with it in registers (no partial stored
+    // for it). Any other partial is counted at the range's end
+    // (count_and_merge).
     const int rows = min(a.RMAX, a.R - s.rb * a.RMAX);  // valid rows of the unit
     const float qnan = __int_as_float(0x7fc00000);
-    if (s.n_parts == 1) {
+    const bool first_seg = ord == 0, last_seg = x >= part.hi;
+    bool own_merge = false;
+    if (s.n_parts == 2 && last_seg && !first_seg) {
+      if (threadIdx.x == 0)
+        s_count = __hip_atomic_load(&a.counters[s.unit], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      own_merge = s_count == 1;  // (uniform) the other part was counted
+      // its stores were acknowledged before its count
+      if (own_merge) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    if (own_merge) {
+      // the other part (the next worker's) into registers: all loads in
+      // flight together, then merged into this part's state in place
+      const int64_t so = (int64_t)s.first_wg + (worker == s.first_wg ? 1 : 0) + s.unit;
+      float2_t mlo[NB], ov[NB][MH][2];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int lrc = min(wave * RW + nb * 16 + c, rows - 1);  // (rows past the unit: never stored)
+        const float* po = a.part_o + (so * a.RMAX + lrc) * H + 4 * g;
+        mlo[nb] = load_coherent2(a.part_ml + (so * a.RMAX + lrc) * 2);
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh) {
+          ov[nb][mh][0] = load_coherent2(po + mh * 16);
+          ov[nb][mh][1] = load_coherent2(po + mh * 16 + 2);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float M0 = bad ? qnan : m[nb];
+        const float Mn = fmaxf(M0, mlo[nb].x);
+        const float w0 = __builtin_amdgcn_exp2f(M0 - Mn), w1 = __builtin_amdgcn_exp2f(mlo[nb].x - Mn);
+        l[nb] = (bad ? qnan : l[nb]) * w0 + mlo[nb].y * w1;
+        m[nb] = Mn;
+#pragma unroll
+        for (int mh = 0; mh < MH; ++mh) {
+          ot[mh][nb][0] = ot[mh][nb][0] * w0 + ov[nb][mh][0].x * w1;
+          ot[mh][nb][1] = ot[mh][nb][1] * w0 + ov[nb][mh][0].y * w1;
+          ot[mh][nb][2] = ot[mh][nb][2] * w0 + ov[nb][mh][1].x * w1;
+          ot[mh][nb][3] = ot[mh][nb][3] * w0 + ov[nb][mh][1].y * w1;
+        }
+      }
+      if (threadIdx.x == 0)
+        __hip_atomic_store(&a.counters[s.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (s.n_parts == 1 || own_merge) {
+      // (a bad part: NaN through its l; a row with no visible key: 0 / 0)
+      const bool nan_out = bad && !own_merge;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int lr = wave * RW + nb * 16 + c;
         if (lr < rows) {
           const int64_t ri = row_index(a, s.b, s.k, s.rb * a.RMAX + lr);
-          const float inv = bad ? qnan : 1.0f / l[nb];
+          const float inv = nan_out ? qnan : 1.0f / l[nb];
 #pragma unroll
           for (int mh = 0; mh < MH; ++mh)
             store_out4(a.out, ri * H + mh * 16 + 4 * g, a.out_dtype, ot[mh][nb][0] * inv, ot[mh][nb][1] * inv,
                        ot[mh][nb][2] * inv, ot[mh][nb][3] * inv);
-          if (g == 0 && a.lse) a.lse[ri] = bad ? qnan : (m[nb] + __log2f(l[nb])) * LN2;
+          if (g == 0 && a.lse) a.lse[ri] = nan_out ? qnan : (m[nb] + __log2f(l[nb])) * LN2;
         }
       }
     } else {
@@ -439,18 +495,33 @@ void attn_wide_kernel(AttnArgs a) {
             store_coherent2(po + lr * H + mh * 16 + 4 * g, bad ? qnan : o[0], bad ? qnan : o[1]);
             store_coherent2(po + lr * H + mh * 16 + 4 * g + 2, bad ? qnan : o[2], bad ? qnan : o[3]);
           }
-          if (g == 0) {
-            store_coherent2(pml + lr * 2, bad ? qnan : m[nb], bad ? qnan : l[nb]);
-          }
+          if (g == 0) store_coherent2(pml + lr * 2, bad ? qnan : m[nb], bad ? qnan : l[nb]);
         }
       }
-      shared.add(s);
+      if (first_seg && !last_seg) {
+        // count now; the rare last count merges at the range's end
+        wait_stores();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          const bool f = count_partial(a, s);
+          if (f) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          s_early = f;
+        }
+        __syncthreads();
+        if (s_early) {
+          early_merge = true;
+          early = s;
+        }
+      } else {
+        shared.add(s);
+      }
     }
   }
   // every copy has landed and been read: the ring is free
   __syncthreads();
   count_and_merge<H, WIDE_ROWS * H / THREADS>(a, shared, s_flag, reinterpret_cast<float*>(ring),
                                               RING_BYTES / 4);
+  if (early_merge) merge_partials<H, WIDE_ROWS * H / THREADS>(a, early, reinterpret_cast<float*>(ring), RING_BYTES / 4);
 }
 
 // ---------------------------------------------------------------- launch
