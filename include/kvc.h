@@ -47,10 +47,13 @@
  *  - The caller owns every buffer. Host-checkable argument errors return a
  *    non-zero status BEFORE anything is launched, so no partial work happens.
  *  - Device metadata cannot be validated on the host without a sync. A
- *    sequence with seq_lens[b] < T or > capacity, or whose block-table entries
- *    needed for its tokens lie outside [0, num_blocks), gets NaN in every
- *    output row (and its append writes nothing); no memory outside the
- *    buffers described here is read or written for it.
+ *    sequence with seq_lens[b] < T or > capacity gets NaN in every output row
+ *    (and its append writes nothing); one whose block-table entries needed
+ *    for its tokens lie outside [0, num_blocks) gets NaN in every output row
+ *    that reads them: every row, except in query blocks of more than 128
+ *    rows per KV head (G * T > 128, chunks of prefill), whose blocks of 128
+ *    rows stop reading at their last row's position under the causal rule.
+ *    No memory outside the buffers described here is read or written.
  *  - Tensor element types are kvc_dtype; K/V caches and q are f16 or bf16.
  */
 #ifndef KVC_H

@@ -8,7 +8,10 @@
 // All units' tiles are laid end to end in (b, k, rb, tile) order and every
 // workgroup takes an equal contiguous share of that flat range, computed on
 // the device from seq_lens (no host read of lengths: "Accelerating Sonar
-// through speculation", section "Inference with speculative decoding").
+// through speculation", section "Inference with speculative decoding"). A
+// unit streams from its first visible key to the last key any of its rows
+// sees: with several row blocks per (b, k), a block of early rows stops
+// before the sequence's end (unit_steps).
 // The range is counted in steps of WAVES tiles (128 tokens): a workgroup's
 // waves take one tile of each step, so they always have equal work; the last
 // step of a unit may hold tiles past its end, which are masked.
@@ -292,9 +295,23 @@ __device__ __forceinline__ int unit_first_step(const AttnArgs& a, int len) {
   return a.window > 0 ? max(0, len - a.T - a.window + 1) / STEP : 0;
 }
 
-// Steps a unit of a sequence of length len streams (0 for invalid lengths).
-__device__ __forceinline__ int unit_steps(const AttnArgs& a, int len) {
-  return seq_valid(len, a.T, a.capacity) ? (len + STEP - 1) / STEP - unit_first_step(a, len) : 0;
+// Steps unit (b, k, rb) of a sequence of length len streams (0 for invalid
+// lengths): from its first visible step to the step holding the last key
+// any of its rows sees. Under the causal rule that is row block rb's last
+// new token (a row block of a long query block stops there; the last row
+// block, and every unit of a single row block, reach the sequence's end);
+// with a tree mask, whose rows may set any bit, the sequence's end.
+__device__ __forceinline__ int unit_steps(const AttnArgs& a, int len, int rb) {
+  if (!seq_valid(len, a.T, a.capacity)) return 0;
+  int end = len;
+  if (!a.tree) end = len - a.T + (min((rb + 1) * a.RMAX, a.R) - 1) / a.G + 1;
+  return (end + STEP - 1) / STEP - unit_first_step(a, len);
+}
+// Steps of the RB units of one (b, k).
+__device__ __forceinline__ int kv_steps(const AttnArgs& a, int len) {
+  int n = 0;
+  for (int rb = 0; rb < a.RB; ++rb) n += unit_steps(a, len, rb);
+  return n;
 }
 
 // First key position a unit's queries can see (0 without a window). Rows
@@ -338,7 +355,7 @@ __device__ __forceinline__ void build_tile_prefix(const AttnArgs& a, int32_t* s_
   for (int i = 0; i < per; ++i) {
     int b = b0 + i;
     if (b < a.B) {
-      local += unit_steps(a, a.seq_lens[b]);
+      local += kv_steps(a, a.seq_lens[b]);
     }
   }
   // inclusive scan of `local` over the workgroup
@@ -360,7 +377,7 @@ __device__ __forceinline__ void build_tile_prefix(const AttnArgs& a, int32_t* s_
       s_pre[b] = run;
       int32_t len = a.seq_lens[b];
       s_pre[a.B + 1 + b] = len;
-      run += unit_steps(a, len);
+      run += kv_steps(a, len);
     }
   }
   if (tid == THREADS - 1) s_pre[a.B] = carry + incl;
@@ -394,7 +411,6 @@ struct Partition {
   int64_t total;  // steps over all units
   int w_eff;      // workers with work: min(W, total); each then has >= 1 step
   int64_t lo, hi; // this worker's flat step range
-  int krb;        // K * RB
   int fast;       // workers with the larger share (0: equal shares)
   int per;        // > 0: fast workers are the first per / 2 of each block of per
   int wf, ws;     // share weights
@@ -439,8 +455,7 @@ __device__ __forceinline__ int worker_of(const AttnArgs& a, int wg) {
 __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int32_t* s_pre,
                                                     int w) {
   Partition p;
-  p.krb = a.K * a.RB;
-  p.total = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[a.B]) * p.krb;
+  p.total = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[a.B]) * a.K;
   p.w_eff = (int)(p.total < (int64_t)a.W ? p.total : (int64_t)a.W);
   // weighted only with at least two steps per worker, so every share keeps
   // at least one step (ws / wf of 2 rounds down to 1); numbered XCD by XCD,
@@ -469,25 +484,33 @@ __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int
 // Segment containing flat step x (x < p.total).
 __device__ __forceinline__ Segment find_segment(const AttnArgs& a, const int32_t* s_pre,
                                                 const Partition& p, int64_t x) {
-  // first b with s_pre[b + 1] * krb > x
+  // first b with s_pre[b + 1] * K > x
   int lo = 0, hi = a.B - 1;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
-    if ((int64_t)s_pre[mid + 1] * p.krb > x) hi = mid; else lo = mid + 1;
+    if ((int64_t)s_pre[mid + 1] * a.K > x) hi = mid; else lo = mid + 1;
   }
   // every field is wave-uniform; readfirstlane keeps them in scalar registers
   Segment s;
   s.b = __builtin_amdgcn_readfirstlane(lo);
   const int p0 = __builtin_amdgcn_readfirstlane(s_pre[s.b]);
-  const int tb = __builtin_amdgcn_readfirstlane(s_pre[s.b + 1]) - p0;
-  const int64_t base = (int64_t)p0 * p.krb;
-  const int off = (int)(x - base);  // < tb * krb
-  const int ur = off / tb;
-  s.k = ur / a.RB;
-  s.rb = ur - s.k * a.RB;
-  s.unit = (s.b * a.K + s.k) * a.RB + s.rb;
+  const int tk = __builtin_amdgcn_readfirstlane(s_pre[s.b + 1]) - p0;  // steps of one (b, k)
+  const int64_t base = (int64_t)p0 * a.K;
+  int off = (int)(x - base);  // < tk * K
+  s.k = off / tk;
+  off -= s.k * tk;
   s.seq_len = __builtin_amdgcn_readfirstlane(s_pre[a.B + 1 + s.b]);
-  s.t_begin = off - ur * tb;
+  // the row block: its units' steps run back to back (off < tk ends the walk)
+  int rb = 0, tb = unit_steps(a, s.seq_len, 0);
+  while (off >= tb) {
+    off -= tb;
+    ++rb;
+    tb = unit_steps(a, s.seq_len, rb);
+  }
+  s.rb = __builtin_amdgcn_readfirstlane(rb);
+  tb = __builtin_amdgcn_readfirstlane(tb);
+  s.unit = (s.b * a.K + s.k) * a.RB + s.rb;
+  s.t_begin = __builtin_amdgcn_readfirstlane(off);
   const int64_t room = p.hi - x;
   s.t_end = (int64_t)(tb - s.t_begin) < room ? tb : s.t_begin + (int)room;
   const int64_t ustart = x - s.t_begin;

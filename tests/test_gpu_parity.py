@@ -174,6 +174,18 @@ def test_run_twice_bitwise(gpu_device):
     assert torch.equal(a.out, b.out) and torch.equal(a.lse, b.lse)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.09, -1.0])
+@pytest.mark.parametrize("shape", [(2, 1, 8, 2, 128), (2, 5, 16, 2, 128), (2, 40, 16, 4, 128)],
+                         ids=["decode", "verify", "long_block"])
+def test_zero_and_negative_scales(gpu_device, scale, shape):
+    """Any finite scale on each of the three kernels: zero (uniform weights
+    over the visible keys) and negative ones (the long-block kernel flips
+    the query's sign bits and folds |scale| into the exponent)."""
+    B, T, N, K, H = shape
+    run = run_case(B, T, N, K, H, BF, [300, 77], seed=90, scale=scale)
+    compare_units(run, all_units(run.inp))
+
+
 def test_scale_one_and_large_scores(gpu_device):
     """The pages' literal product (no scale) with N(0,1) inputs at H = 128 gives
     scores with sd ~ 11: the softmax is nearly one-hot."""
@@ -740,7 +752,15 @@ def test_long_causal_tree_rows_are_the_plain_verify(gpu_device, case):
     kw = dict(seed=710, num_workgroups=17)
     plain = run_case(B, T, N, K, H, dtype, prior, **kw)
     tree = run_case(B, T, N, K, H, dtype, prior, tree=[causal_tree_words(T)] * B, **kw)
-    assert torch.equal(plain.out, tree.out) and torch.equal(plain.lse, tree.lse)
+    if (N // K) * T <= 128:
+        assert torch.equal(plain.out, tree.out) and torch.equal(plain.lse, tree.lse)
+    else:
+        # several row blocks: without a tree each one stops streaming at its
+        # last row's key, with one (any bit may be set) at the sequence's
+        # end, so the two runs split the work differently; equal to fp32
+        # rounding
+        assert float((plain.out - tree.out).abs().max()) <= 1e-5
+        assert float((plain.lse - tree.lse).abs().max()) <= 1e-5
 
 
 @pytest.mark.parametrize("fused", [False, True])
