@@ -146,6 +146,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (;;) {
       const int64_t x = cs.x;
       const bool more = x + 1 < part.hi;
+      // The two workgroups of a CU (i and i + W / 2 in an automatic grid)
+      // take turns at the higher wave priority, step by step: the hardware
+      // otherwise serves the older one first throughout.
+      if ((x + (blockIdx.x >= gridDim.x / 2 ? 1 : 0)) & 1)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
       const char* kslot = ring;
       const char* vslot = ring + VSLOT;
       // ---- K half of step x: the one later copy is its V half
