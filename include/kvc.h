@@ -327,6 +327,24 @@ const char *kvc_status_string(int status);
 kvc_status kvc_gather(const kvc_cache *paged, void *dst_k, void *dst_v, int B, int K, int H,
                       const int32_t *seq_lens, int max_seq_len, void *stream);
 
+/*
+ * Test export (host only, nothing is launched): the flat step ranges that
+ * the attention kernels give their workers, computed by the kernels' own
+ * partition code. `total` steps over W workers; fast_workers, xcds,
+ * share_fast, share_slow, xcd_even and xcd_odd as a launch plan sets them
+ * (fast_workers 0: equal shares; xcds 0: workers in launch order; xcd_even
+ * or xcd_odd 0: no XCD factors). Writes lo_hi[2w] and lo_hi[2w + 1], the
+ * range [lo, hi) of worker w, for every w < W (caller-owned, 2W entries)
+ * and, when owners is not NULL, owners[x] for every x < total (caller-owned,
+ * total entries): the worker the kernels take as holding step x when they
+ * look up another worker's part of a unit. KVC_ERR_INVALID for total outside
+ * [0, 2^32], W outside [1, 2^20], negative fast_workers or xcds, share
+ * weights outside [1, 16], XCD factors outside [0, 64], or lo_hi NULL.
+ */
+kvc_status kvc_partition_ranges(int64_t total, int W, int fast_workers, int xcds, int share_fast,
+                                int share_slow, int xcd_even, int xcd_odd, int64_t *lo_hi,
+                                int32_t *owners);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,7 @@ EXPORTS = (
     "kvc_plan_kernel",
     "kvc_status_string",
     "kvc_gather",
+    "kvc_partition_ranges",
 )
 
 
@@ -117,6 +118,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvc_status_string.restype = ctypes.c_char_p
     lib.kvc_gather.argtypes = [cache_p, vp, vp, c_int, c_int, c_int, vp, c_int, vp]
     lib.kvc_gather.restype = c_int
+    lib.kvc_partition_ranges.argtypes = [ctypes.c_int64, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                         vp, vp]
+    lib.kvc_partition_ranges.restype = c_int
     if path is None:
         _lib = lib
     return lib

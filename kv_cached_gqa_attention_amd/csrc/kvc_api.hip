@@ -87,6 +87,7 @@ struct Plan {
   int W;        // workgroups launched
   int fast;     // workers given the larger share (see Partition), 0: equal shares
   int share_fast, share_slow;  // the shares' weights
+  int xcd_even, xcd_odd;       // share factors by XCD parity (0: none)
   int xcds;     // workers numbered XCD by XCD (see worker_of), 0: in launch order
   int workers;  // independent workers: waves (vector-ALU kernel) or workgroups (matrix cores)
   size_t off_o, off_ml, bytes;
@@ -151,6 +152,9 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
   // kernels, about 20% on the long-block kernel
   p->share_fast = p->wide ? 6 : 5;
   p->share_slow = p->wide ? 5 : 4;
+  // the odd-numbered XCD of each pair streams about 6% slower
+  p->xcd_even = xcds > 1 && xcds % 2 == 0 ? 16 : 0;
+  p->xcd_odd = xcds > 1 && xcds % 2 == 0 ? 15 : 0;
   p->workers = p->W * per_wg;
   const size_t slots = (size_t)p->workers + (size_t)p->units;
   p->off_ml = (size_t)COUNTER_SLOTS * sizeof(int32_t);
@@ -315,6 +319,8 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   a.fast_workers = p.fast;
   a.share_fast = p.share_fast;
   a.share_slow = p.share_slow;
+  a.xcd_even = p.xcd_even;
+  a.xcd_odd = p.xcd_odd;
   a.xcds = p.xcds;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.window = window;
@@ -464,6 +470,27 @@ kvc_status kvc_gather(const kvc_cache* paged, void* dst_k, void* dst_v, int B, i
   a.max_seq_len = max_seq_len;
   const hipError_t e = kvc::launch_gather(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+kvc_status kvc_partition_ranges(int64_t total, int W, int fast_workers, int xcds, int share_fast,
+                                int share_slow, int xcd_even, int xcd_odd, int64_t* lo_hi,
+                                int32_t* owners) {
+  if (total < 0 || total > ((int64_t)1 << 32) || W < 1 || W > (1 << 20) || fast_workers < 0 ||
+      xcds < 0 || share_fast < 1 || share_fast > 16 || share_slow < 1 || share_slow > 16 ||
+      xcd_even < 0 || xcd_even > 64 || xcd_odd < 0 || xcd_odd > 64 || !lo_hi)
+    return KVC_ERR_INVALID;
+  for (int w = 0; w < W; ++w) {
+    const kvc::Partition p = kvc::partition_of(total, W, fast_workers, xcds, share_fast, share_slow,
+                                               xcd_even, xcd_odd, w);
+    lo_hi[2 * w] = p.lo;
+    lo_hi[2 * w + 1] = p.hi;
+  }
+  if (owners && total > 0) {
+    const kvc::Partition p = kvc::partition_of(total, W, fast_workers, xcds, share_fast, share_slow,
+                                               xcd_even, xcd_odd, 0);
+    for (int64_t x = 0; x < total; ++x) owners[x] = p.owner(x);
+  }
+  return KVC_OK;
 }
 
 }  // extern "C"

@@ -70,6 +70,8 @@ struct AttnArgs {
   int32_t fast_workers;  // workers with the larger share (0: equal shares; see Partition)
   int32_t share_fast;    // the larger and the smaller share's weights
   int32_t share_slow;
+  int32_t xcd_even;      // share factors of workers on even- and odd-numbered
+  int32_t xcd_odd;       // XCDs (0: not weighted; see Partition)
   int32_t xcds;       // > 0: workers numbered XCD by XCD (worker_of); 0: worker = workgroup
   float scale_log2;   // scale * log2(e)
   float* part_o;      // [W + units, RMAX, H], slot = worker + unit
@@ -398,44 +400,68 @@ struct Segment {
   int first_wg;   // first worker sharing the unit
 };
 
-// Workers' shares of the steps: equal, or (fast > 0) weighted wf : ws
-// between the older and the younger workgroup of each CU. With two
+// Workers' shares of the steps: equal, or (fast > 0) weighted. With two
 // workgroups per CU (a full round of 2 x CUs) the first `fast` = CUs
 // workgroups are each the older of a CU's pair, and the older one is served
 // first (about 25% faster on the decode kernels, about 20% on the long-block
-// kernel); weighting the shares lets both finish together. In launch order
-// (per = 0) the fast workers are workers [0, fast); numbered XCD by XCD
-// (worker_of, per = W / xcds workers per XCD) they are the first half of
-// each XCD's block.
+// kernel): its share is weighted wf against the younger one's ws. In launch
+// order (per = 0) the fast workers are workers [0, fast); numbered XCD by
+// XCD (worker_of, per = W / xcds workers per XCD) they are the first half of
+// each XCD's block. On top of that, a worker's share is multiplied by xe on
+// an even-numbered XCD and by xo on an odd-numbered one (the odd XCD of each
+// pair streams a few percent slower; 1 : 1 when not weighted). Workgroup i
+// runs on XCD i mod xcds with xcds even, so in launch order worker w's XCD
+// has the parity of w, and in XCD order that of its block w / per.
 struct Partition {
   int64_t total;  // steps over all units
   int w_eff;      // workers with work: min(W, total); each then has >= 1 step
   int64_t lo, hi; // this worker's flat step range
   int fast;       // workers with the larger share (0: equal shares)
   int per;        // > 0: fast workers are the first per / 2 of each block of per
-  int wf, ws;     // share weights
+  int wf, ws;     // share weights of the older and the younger workgroup
+  int xe, xo;     // share factors on even- and odd-numbered XCDs
   int64_t wt;     // sum of the shares (w_eff when equal)
 
-  __device__ int64_t share_prefix(int w) const {  // shares of workers [0, w)
-    if (!fast) return w;
+  // XCD factors of launch-order workers [0, n) (even ones xe, odd ones xo),
+  // and its inverse: the largest n with xsum(n) <= v
+  __host__ __device__ int64_t xsum(int64_t n) const { return (n + 1) / 2 * xe + n / 2 * xo; }
+  __host__ __device__ int64_t xinv(int64_t v) const {
+    const int64_t m = v / (xe + xo), r = v - m * (xe + xo);
+    return 2 * m + (r >= xe ? 1 : 0);
+  }
+  __host__ __device__ int64_t share_prefix(int w) const {  // shares of workers [0, w)
     if (per) {
-      const int h = per >> 1, r = w % per;
-      return (int64_t)(w / per) * h * (wf + ws) + (int64_t)min(r, h) * wf + (int64_t)max(r - h, 0) * ws;
+      const int h = per >> 1, r = w % per, blk = w / per;
+      const int64_t be = (int64_t)h * (wf + ws) * xe, bo = (int64_t)h * (wf + ws) * xo;
+      return (int64_t)(blk >> 1) * (be + bo) + (blk & 1 ? be : 0) +
+             (int64_t)(blk & 1 ? xo : xe) * ((int64_t)(r < h ? r : h) * wf + (int64_t)(r > h ? r - h : 0) * ws);
     }
-    return w <= fast ? (int64_t)wf * w : (int64_t)wf * fast + (int64_t)ws * (w - fast);
+    if (!fast) return xsum(w);
+    const int64_t sf = xsum(w < fast ? w : fast);
+    return wf * sf + ws * (xsum(w) - sf);
   }
   // Worker w's range is [total * P(w) / wt, total * P(w + 1) / wt), P the
   // share prefix; the owner of step x is the largest w with P(w) <= u.
-  __device__ int owner(int64_t x) const {  // worker whose range holds step x
+  __host__ __device__ int owner(int64_t x) const {  // worker whose range holds step x
     const int64_t u = ((x + 1) * wt - 1) / total;
-    if (!fast) return (int)u;
     int64_t w;
     if (per) {
       const int h = per >> 1;
-      const int64_t bw = (int64_t)h * (wf + ws), blk = u / bw, rem = u - blk * bw;
-      w = blk * per + (rem < (int64_t)h * wf ? rem / wf : h + (rem - (int64_t)h * wf) / ws);
+      const int64_t be = (int64_t)h * (wf + ws) * xe, bo = (int64_t)h * (wf + ws) * xo;
+      const int64_t pr = u / (be + bo);
+      int64_t rem = u - pr * (be + bo), blk = 2 * pr, xs = xe;
+      if (rem >= be) {
+        blk += 1;
+        rem -= be;
+        xs = xo;
+      }
+      const int64_t hf = (int64_t)h * wf * xs;
+      w = blk * per + (rem < hf ? rem / (wf * xs) : h + (rem - hf) / (ws * xs));
+    } else if (!fast) {
+      w = xinv(u);
     } else {
-      w = u < (int64_t)wf * fast ? u / wf : fast + (u - (int64_t)wf * fast) / ws;
+      const int64_t sf = xsum(fast);
+      w = u < wf * sf ? xinv(u / wf) : xinv(sf + (u - wf * sf) / ws);
     }
     return (int)(w < w_eff - 1 ? w : w_eff - 1);
   }
@@ -452,26 +478,42 @@ __device__ __forceinline__ int worker_of(const AttnArgs& a, int wg) {
   return (wg % a.xcds) * per + wg / a.xcds;
 }
 
-__device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int32_t* s_pre,
-                                                    int w) {
+// Worker w's partition of `total` steps over W workers, with the launch's
+// weighting (fast_workers, xcds, the share weights and XCD factors as in
+// AttnArgs). Host-callable for the checks of the test export.
+__host__ __device__ inline Partition partition_of(int64_t total, int W, int fast_workers, int xcds,
+                                                  int share_fast, int share_slow, int xcd_even,
+                                                  int xcd_odd, int w) {
   Partition p;
-  p.total = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[a.B]) * a.K;
-  p.w_eff = (int)(p.total < (int64_t)a.W ? p.total : (int64_t)a.W);
-  // weighted only with at least two steps per worker, so every share keeps
-  // at least one step (ws / wf of 2 rounds down to 1); numbered XCD by XCD,
-  // only with every worker busy (the block structure)
-  p.fast = a.fast_workers > 0 && a.fast_workers < p.w_eff && p.total >= 2 * (int64_t)p.w_eff
-               ? a.fast_workers : 0;
+  p.total = total;
+  p.w_eff = (int)(p.total < (int64_t)W ? p.total : (int64_t)W);
+  // weighted only with at least two steps per worker (and, below, only where
+  // every weighted share keeps at least one step); numbered XCD by XCD, only
+  // with every worker busy (the block structure)
+  p.fast = fast_workers > 0 && fast_workers < p.w_eff && p.total >= 2 * (int64_t)p.w_eff
+               ? fast_workers : 0;
   p.per = 0;
-  if (p.fast && a.xcds > 0) {
-    if (p.w_eff == a.W && a.W == 2 * a.fast_workers && a.fast_workers % a.xcds == 0)
-      p.per = a.W / a.xcds;
+  if (p.fast && xcds > 0) {
+    if (p.w_eff == W && W == 2 * fast_workers && fast_workers % xcds == 0)
+      p.per = W / xcds;
     else
       p.fast = 0;
   }
-  p.wf = a.share_fast;
-  p.ws = a.share_slow;
+  p.wf = share_fast;
+  p.ws = share_slow;
+  // the XCD factors only with the weighted shares of a full round (an even
+  // number of fast workers keeps the parity pattern of launch order)
+  const bool xw = p.fast && xcd_even > 0 && xcd_odd > 0 && (p.per || p.fast % 2 == 0);
+  p.xe = xw ? xcd_even : 1;
+  p.xo = xw ? xcd_odd : 1;
   p.wt = p.share_prefix(p.w_eff);
+  // every worker keeps at least one step: otherwise equal shares
+  const int64_t wmin = (int64_t)(p.wf < p.ws ? p.wf : p.ws) * (p.xe < p.xo ? p.xe : p.xo);
+  if (p.fast && p.total * wmin < p.wt) {
+    p.fast = p.per = 0;
+    p.xe = p.xo = 1;
+    p.wt = p.share_prefix(p.w_eff);
+  }
   if (w < p.w_eff) {
     p.lo = p.total * p.share_prefix(w) / p.wt;
     p.hi = p.total * p.share_prefix(w + 1) / p.wt;
@@ -479,6 +521,13 @@ __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int
     p.lo = p.hi = 0;
   }
   return p;
+}
+
+__device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int32_t* s_pre,
+                                                    int w) {
+  const int64_t total = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[a.B]) * a.K;
+  return partition_of(total, a.W, a.fast_workers, a.xcds, a.share_fast, a.share_slow, a.xcd_even,
+                      a.xcd_odd, w);
 }
 
 // Segment containing flat step x (x < p.total).
