@@ -173,6 +173,8 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   StepCursor cs;
   cs.begin(a, s_pre, part, part.lo, wave);
   SharedUnits shared;
+  Segment early;             // a unit whose early part was counted last
+  bool early_merge = false;  // (uniform)
   while (true) {
     const Segment s = cs.s;
     // Q^T fragments (B operand): query row rb*RMAX + 16 nb + c, h = 32 ks + 8 g + j.
@@ -395,7 +397,28 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    finish_segment<H, 1, OST>(a, s, worker, s_m, s_l, s_o, s_m, segbad, shared);
+    if (s.n_parts > 1 && cs.ord == 0 && cs.x + 1 < part.hi) {
+      // The range's first segment, not its last: the later steps of a unit
+      // shared with the worker before, done early. Its partial is counted
+      // now, so that the worker holding the unit's first steps (done last)
+      // merges it; if this count is the last (rare), the merge waits for the
+      // range's end.
+      store_partial<H, 1, OST>(a, s, worker, s_m, s_l, s_o, s_m, segbad);
+      wait_stores();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const bool f = count_partial(a, s);
+        if (f) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_flag[0] = f;
+      }
+      __syncthreads();
+      if (s_flag[0]) {
+        early_merge = true;
+        early = s;
+      }
+    } else {
+      finish_segment<H, 1, OST>(a, s, worker, s_m, s_l, s_o, s_m, segbad, shared);
+    }
     if (cs.x + 1 >= part.hi) break;
     cs.advance(a, s_pre, part);
   }
@@ -403,6 +426,9 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   __syncthreads();
   count_and_merge<H, (RMAX * H + THREADS - 1) / THREADS>(a, shared, s_flag, reinterpret_cast<float*>(ring_all),
                      WAVES * nslots * TILEB / 4);
+  if (early_merge)
+    merge_partials<H, (RMAX * H + THREADS - 1) / THREADS>(a, early, reinterpret_cast<float*>(ring_all),
+                                                          WAVES * nslots * TILEB / 4);
 }
 
 // ---------------------------------------------------------------- launch
