@@ -123,6 +123,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   cn.advance(a, s_pre, part);
 
   SharedUnits shared;
+  Segment early;             // a unit whose early part was counted last
+  bool early_merge = false;  // (uniform)
   while (true) {
     // ---- a new segment: its masks and state
     const Segment g = cs.s;
@@ -301,7 +303,28 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bool segbad = false;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) segbad |= s_bad[w] != 0;
-    finish_segment<H, WAVES>(a, g, worker, s_m, s_l, s_o, s_w, segbad, shared);
+    if (g.n_parts > 1 && cs.ord == 0 && cs.x + 1 < part.hi) {
+      // The range's first segment, not its last: the later steps of a unit
+      // shared with the worker before, done early. Its partial is counted
+      // now (the wait drains the next segment's copies in flight, once per
+      // range), so that the worker holding the unit's first steps merges it;
+      // if this count is the last (rare), the merge waits for the range's end.
+      store_partial<H, WAVES>(a, g, worker, s_m, s_l, s_o, s_w, segbad);
+      wait_stores();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const bool f = count_partial(a, g);
+        if (f) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_flag[0] = f;
+      }
+      __syncthreads();
+      if (s_flag[0]) {
+        early_merge = true;
+        early = g;
+      }
+    } else {
+      finish_segment<H, WAVES>(a, g, worker, s_m, s_l, s_o, s_w, segbad, shared);
+    }
 
     if (cs.x + 1 >= part.hi) break;
     cs.advance(a, s_pre, part);
@@ -309,6 +332,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // every copy has landed and every slot has been read: the slots are free
   __syncthreads();
   count_and_merge<H, (R * H + THREADS - 1) / THREADS>(a, shared, s_flag,
+                     reinterpret_cast<float*>(reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B)),
+                     valu_ring_bytes<H>() / 4);
+  if (early_merge)
+    merge_partials<H, (R * H + THREADS - 1) / THREADS>(a, early,
                      reinterpret_cast<float*>(reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B)),
                      valu_ring_bytes<H>() / 4);
 }

@@ -660,11 +660,11 @@ __device__ __forceinline__ void fill_invalid(const AttnArgs& a, const int32_t* s
 // its whole range is done (count_and_merge): the workgroup that counts a
 // unit's last partial merges them all (merge_partials). Waiting for the
 // partial stores and for the count's return only once per worker, at its
-// end, keeps both latencies out of the middle of the range. (The
-// matrix-core kernels count the partial of a range's first segment, the
-// later steps of a unit shared with the worker before, at once instead: the
-// worker holding that unit's first steps, which it does last, then merges
-// it, and no workgroup ends with two merges.) `bad` marks a
+// end, keeps both latencies out of the middle of the range. (The kernels
+// count the partial of a range's first segment, the later steps of a unit
+// shared with the worker before, at once instead: the worker holding that
+// unit's first steps, which it does last, then merges it, and no workgroup
+// ends with two merges.) `bad` marks a
 // segment that met an out-of-range block-table entry: its result is NaN.
 
 // Per row r < rows: the largest of the NW waves' maxima, each wave's weight
