@@ -302,12 +302,12 @@ void attn_wide_kernel(AttnArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- S^T = K . Q^T
+      // ---- S^T = K . Q^T, row block 0 first
       floatx4 st[2][NB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int mb = 0; mb < 2; ++mb) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) acc = mfma16<BF>(kf[mb][ks], qv[nb][ks], acc);
@@ -341,33 +341,26 @@ void attn_wide_kernel(AttnArgs a) {
       // maximum where that is larger, and the weights are taken again.
       uint4 phi[NB], plo[NB];
       float tsum[NB];
-      auto weights = [&]() __attribute__((always_inline)) {
+      auto weights = [&](int nb) __attribute__((always_inline)) {
+        uint32_t hw[4], lw[4];
+        float ps[4];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          uint32_t hw[4], lw[4];
-          float ps[4];
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; i4 += 2) {
-              // a masked score (-inf) gives exp2(-inf) = 0 (c > 0)
-              const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4], sc, -m[nb]));
-              const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4 + 1], sc, -m[nb]));
-              ps[mb * 2 + i4 / 2] = e0 + e1;
-              split_pair_fast<BF>(e0, e1, skc, hw[mb * 2 + i4 / 2], lw[mb * 2 + i4 / 2]);
-            }
-          tsum[nb] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-          phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        }
+          for (int i4 = 0; i4 < 4; i4 += 2) {
+            // a masked score (-inf) gives exp2(-inf) = 0 (c > 0)
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4], sc, -m[nb]));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[mb][nb][i4 + 1], sc, -m[nb]));
+            ps[mb * 2 + i4 / 2] = e0 + e1;
+            split_pair_fast<BF>(e0, e1, skc, hw[mb * 2 + i4 / 2], lw[mb * 2 + i4 / 2]);
+          }
+        tsum[nb] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       };
-      weights();
-      bool over = false;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) over |= !(tsum[nb] <= WEIGHT_BOUND);  // (NaN: over)
-      if (__builtin_amdgcn_ballot_w64(over) != 0ull) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+      auto settle = [&](int nb) __attribute__((always_inline)) {
+        // (NaN: over the bound)
+        if (__builtin_amdgcn_ballot_w64(!(tsum[nb] <= WEIGHT_BOUND)) != 0ull) {
           float p8[8];
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
@@ -382,21 +375,25 @@ void attn_wide_kernel(AttnArgs a) {
 #pragma unroll
           for (int mh = 0; mh < MH; ++mh) ot[mh][nb] *= alpha;
           m[nb] = mn;
+          weights(nb);
         }
-        weights();
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) l[nb] += tsum[nb];
-
+        l[nb] += tsum[nb];
+      };
       // ---- O^T += V^T . P^T
+      auto pv = [&](int nb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int mh = 0; mh < MH; ++mh) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int mh = 0; mh < MH; ++mh) {
           ot[mh][nb] = mfma16<BF>(vf[mh], phi[nb], ot[mh][nb]);
           ot[mh][nb] = mfma16<BF>(vf[mh], plo[nb], ot[mh][nb]);
         }
-      }
+      };
+      // block by block: one block's products overlap the other's weights
+      weights(0);
+      settle(0);
+      pv(0);
+      weights(1);
+      settle(1);
+      pv(1);
       cslot = cslot + 1 == NR ? 0 : cslot + 1;
     }
 
