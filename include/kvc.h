@@ -230,7 +230,10 @@ kvc_status kvc_append_attend(const kvc_cache *cache, const void *k_new, const vo
  *   before that position are not read and those blocks may be unmapped or
  *   reused: the cache a windowed call needs does not grow with the sequence
  *   ("Stanford CS336 Day 13 - Inference", "Local Attention": rows that left
- *   the window can leave the cache).
+ *   the window can leave the cache). A rolling cache is a cyclic table:
+ *   logical block j of a sequence in ring[j mod R], R blocks covering at
+ *   least W + T - 1 + 2 * block_size positions, so that the append of the
+ *   new rows overwrites only positions the window no longer needs.
  * tree_mask: NULL for the causal rule inside the block, or device
  *   [B, T, TW] uint32 words, TW = (T + 31) / 32, for draft-tree verification
  *   ("Accelerating Sonar through speculation", section "EAGLE": tree-shaped

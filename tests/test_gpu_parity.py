@@ -690,6 +690,55 @@ def test_window_never_reads_blocks_before_it(gpu_device, T, N, K, H):
     compare_units(run, all_units(inp))
 
 
+@pytest.mark.parametrize("T,N,K,H,fused", [(1, 32, 8, 128, False), (1, 32, 8, 128, True),
+                                           (5, 64, 8, 128, False), (3, 8, 2, 64, True)])
+def test_window_over_a_ring_of_blocks(gpu_device, T, N, K, H, fused):
+    """A rolling cache of a few blocks per sequence for local attention: the
+    block table maps logical block j of sequence b to ring[b][j mod R], so
+    every new block overwrites the oldest one. R blocks hold the W + T - 1
+    positions a window of W needs; the prior rows are written through the
+    ring in order (older positions overwritten), the library appends the new
+    rows into it, and the windowed call matches the oracle over the whole
+    logical sequence."""
+    B, W, bs = 3, 100, 16
+    R = -(-(W + T - 1) // bs) + 2  # blocks the window can touch, plus a spare
+    inp = draw_inputs(B, T, N, K, H, BF, np.array([1000, 77, 513]), 540 + T, device="cpu")
+    dev = gpu_device
+    for name in ("q", "k_new", "v_new", "ctx_k", "ctx_v"):
+        setattr(inp, name, getattr(inp, name).to(dev))
+    nb_max = int(-(-inp.seq_lens.max() // bs))
+    ring = np.random.Generator(np.random.PCG64(541)).permutation(B * R + 3).astype(np.int32)[: B * R].reshape(B, R)
+    table = np.stack([ring[b][np.arange(nb_max) % R] for b in range(B)]).astype(np.int32)
+    shape = (B * R + 3, K, bs, H)
+    pk = torch.full(shape, float("nan"), dtype=BF, device=dev)
+    pv = torch.full(shape, float("nan"), dtype=BF, device=dev)
+    for b in range(B):
+        P = int(inp.prior[b])
+        s, e = int(inp.ctx_off[b]), int(inp.ctx_off[b + 1])
+        # the positions the ring still holds: those of its last R - 1 blocks
+        # and the block being filled (each slot written once)
+        start = max(0, (P // bs - (R - 1)) * bs)
+        t = torch.arange(start, P, device=dev)
+        blk = torch.from_numpy(table[b]).to(dev)[t // bs].long()
+        pk[blk, :, t % bs, :] = inp.ctx_k[s + start : e]
+        pv[blk, :, t % bs, :] = inp.ctx_v[s + start : e]
+    cache = kvc.Cache(pk, pv, torch.from_numpy(table).to(dev))
+    seq_lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).to(dev)
+    L = int(inp.seq_lens.max())
+    q = inp.q[:, 0].contiguous() if T == 1 else inp.q
+    kw = dict(k_new=inp.k_new, v_new=inp.v_new) if fused else {}
+    if not fused:
+        kvc.append(cache, inp.k_new, inp.v_new, seq_lens)
+    out, lse = kvc.attend(q, cache, seq_lens, L, window=W, out_dtype=torch.float32, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    if T == 1:
+        out, lse = out[:, None], lse[:, None]
+    from gpu_cases import Run
+
+    run = Run(inp, cache, seq_lens, out, lse, 1 / math.sqrt(H), window=W)
+    compare_units(run, all_units(inp))
+
+
 def test_default_workspace_is_per_stream_and_refused_under_capture(gpu_device):
     """Calls without an explicit workspace on two streams get two buffers (so
     overlapping calls never share counters); a larger call on one stream
