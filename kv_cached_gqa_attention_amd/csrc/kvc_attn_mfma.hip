@@ -35,21 +35,14 @@ namespace kvc {
 template <int H>
 constexpr int mfma_tile_bytes() { return TILE * H * 2; }
 
-// Whether two workgroups of the QLDS form fit one CU's LDS: per workgroup
-// the prefix table, the unit's query rows and two slots per wave, the wave
-// fold living in the slots (under 1 KB of other LDS).
-__host__ __device__ constexpr bool mfma_two_per_cu(int B, int H, int RMAX) {
-  return RMAX <= 48 && prefix_bytes(B) + (size_t)RMAX * H * 2 + (size_t)WAVES * 2 * TILE * H * 2 + 1024 <= 80 * 1024;
-}
-
 // MASKED: a window or draft-tree mask is in use (the general per-key test);
 // otherwise the causal test alone. nslots: staging slots per wave (2 or 3).
-// QLDS: two workgroups per CU (two waves per SIMD, so one wave's waits hide
-// under the other's work). To fit, the query rows live in LDS rather than
-// in registers, the copies stop at each unit boundary, and the waves' fold
-// at a unit's end reuses the slots.
-template <bool BF, int H, int NB, bool PAGED, bool MASKED, bool QLDS>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(QLDS ? 2 : 1, QLDS ? 2 : 1)))
+// One workgroup per CU (one wave per SIMD): the query rows stay in registers
+// for a whole segment and the copies run on across unit boundaries. (A form
+// with two workgroups per CU, the query rows in LDS and the copies stopping
+// at each unit boundary, measured 1-4% slower on every verify shape.)
+template <bool BF, int H, int NB, bool PAGED, bool MASKED>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma_kernel(AttnArgs a, int nslots) {
   constexpr int RMAX = NB * 16;  // query rows per unit (row block)
   // Row stride (floats) of the waves' fold in LDS: H + 4 puts the 16 query
@@ -62,10 +55,10 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   constexpr int NI = TILE * ROWB / 1024;  // copy instructions per tile
   constexpr int TILEB = mfma_tile_bytes<H>();
 
-  // [2B + 1], (QLDS: the unit's query rows,) then the slots
+  // [2B + 1], then the slots
   extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];
   __shared__ float s_m[RMAX], s_l[RMAX];
-  __shared__ float s_o_own[QLDS ? 4 : RMAX * OST];
+  __shared__ float s_o[RMAX * OST];  // the waves' fold
   __shared__ int32_t s_wave[WAVES], s_bad[WAVES], s_flag[2];
 
   build_tile_prefix(a, s_pre, s_wave);
@@ -79,10 +72,8 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int c = lane & 15;   // column (query row) / A-row (token or h) within a 16 block
   const int g = lane >> 4;   // k-slot group
-  char* qarea = reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B);  // QLDS: RMAX rows, swizzled as K
-  char* ring_all = qarea + (QLDS ? RMAX * ROWB : 0);
+  char* ring_all = reinterpret_cast<char*>(s_pre) + prefix_bytes(a.B);
   char* ring = ring_all + wave * nslots * TILEB;
-  float* s_o = QLDS ? reinterpret_cast<float*>(ring_all) : s_o_own;  // the waves' fold
   const uint32_t ring_lds = lds_addr(ring);
   const lds_char* ring3 = (const lds_char*)ring;
 
@@ -114,7 +105,6 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   }
 
   // ---- copies: halves K(x), V(x) of steps x = lo, lo + 1, ... in slot order
-  // (QLDS: restarted at every unit boundary)
   int nhalves = (int)(2 * (part.hi - part.lo));
   int hp = 0;         // halves issued
   int pslot = 0;      // slot of the next one
@@ -139,7 +129,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   auto prologue = [&]() __attribute__((always_inline)) {
     for (int i = 0; i < nslots && hp < nhalves; ++i) issue_next();
   };
-  if (!QLDS) prologue();
+  prologue();
   int hc = 0;      // halves consumed
   int cslot = 0;   // slot of the next one
   // Wait for half hc + ahead: the halves issued after it are in flight (at
@@ -168,7 +158,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
       for (int ks = 0; ks < KS; ++ks)
         kf[mb][ks] = *reinterpret_cast<const uint4*>(kt + koff[ks] + mb * 16 * ROWB);
   };
-  if (!QLDS) read_k(0);
+  read_k(0);
 
   StepCursor cs;
   cs.begin(a, s_pre, part, part.lo, wave);
@@ -178,7 +168,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
   while (true) {
     const Segment s = cs.s;
     // Q^T fragments (B operand): query row rb*RMAX + 16 nb + c, h = 32 ks + 8 g + j.
-    uint4 qf[QLDS ? 1 : NB][KS];
+    uint4 qf[NB][KS];
     int tq[NB];         // new-token index of this lane's query column
     // its tree-mask row: T <= RMAX <= 64 new tokens, so at most two words
     uint32_t tw[NB], tw1[NB];
@@ -186,17 +176,13 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
     for (int nb = 0; nb < NB; ++nb) {
       const int rr = s.rb * RMAX + nb * 16 + c;
       if (rr < a.R) {
-        if constexpr (!QLDS) {
-          const char* qrow = a.q + row_index(a, s.b, s.k, rr) * (H * 2);
+        const char* qrow = a.q + row_index(a, s.b, s.k, rr) * (H * 2);
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = load16(qrow + (ks * 32 + g * 8) * 2);
-        }
+        for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = load16(qrow + (ks * 32 + g * 8) * 2);
         tq[nb] = rr / a.G;
       } else {
-        if constexpr (!QLDS) {
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = make_uint4(0, 0, 0, 0);
-        }
+        for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = make_uint4(0, 0, 0, 0);
         tq[nb] = a.T - 1;  // padding column: any valid row, discarded
       }
       const uint32_t* trow = MASKED && a.tree ? a.tree + ((int64_t)s.b * a.T + tq[nb]) * a.tree_words : nullptr;
@@ -206,29 +192,6 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
     // Every outstanding load (these and the copies in flight) has landed,
     // so no wait for the query loads falls inside the tile loop.
     wait_stores();
-    if constexpr (QLDS) {
-      // this unit's copies, and its query rows: RMAX rows of ROWB bytes,
-      // chunk j of row r at position j ^ swz_k(r) (rows past R repeat row
-      // R - 1; their columns are discarded); each wave copies a quarter
-      hp = hc = pslot = cslot = 0;
-      pv = false;
-      pc = cs;
-      nhalves = (int)(2 * (cs.end - cs.x));
-      prologue();
-      constexpr int QI = RMAX * ROWB / 1024 / WAVES;  // copy instructions per wave
-      static_assert(RMAX * ROWB % (1024 * WAVES) == 0, "query rows split evenly");
-#pragma unroll
-      for (int i = 0; i < QI; ++i) {
-        const int q = (wave * QI + i) * 64 + lane;  // 16-byte chunk of the area
-        const int r = q / (ROWB / 16);
-        const int j = (q % (ROWB / 16)) ^ swz_k(r);
-        const int rr = min(s.rb * RMAX + r, a.R - 1);
-        dma16_addr(a.q + row_index(a, s.b, s.k, rr) * ROWB + j * 16,
-                   lds_addr(qarea) + (wave * QI + i) * 1024);
-      }
-      wait_vm<0>();
-      __syncthreads();
-    }
 
     floatx4 ot[MH][NB];
 #pragma unroll
@@ -244,8 +207,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
     const int new0 = s.seq_len - a.T;
 
     for (;;) {
-      // ---- S^T = K . Q^T (one wave per SIMD: K was read a tile ahead)
-      if constexpr (QLDS) read_k(0);
+      // ---- S^T = K . Q^T (K was read a tile ahead)
       floatx4 st[2][NB];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -253,14 +215,7 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
         for (int nb = 0; nb < NB; ++nb) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if constexpr (QLDS) {
-              const uint4 qv = *reinterpret_cast<const uint4*>(qarea + nb * 16 * ROWB + koff[ks]);
-              acc = mfma16<BF>(kf[mb][ks], qv, acc);
-            } else {
-              acc = mfma16<BF>(kf[mb][ks], qf[nb][ks], acc);
-            }
-          }
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16<BF>(kf[mb][ks], qf[nb][ks], acc);
           st[mb][nb] = acc;
         }
       release_half();
@@ -323,8 +278,8 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
         phi[nb] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         plo[nb] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
-      // ---- V^T of this tile, and (one wave per SIMD) the next tile's K,
-      // possibly of the next unit, read before the p.v products
+      // ---- V^T of this tile, and the next tile's K, possibly of the next
+      // unit, read before the p.v products
       wait_half(0);
       const lds_char* vt_base = ring3 + cslot * TILEB;
       auto read_v = [&](int mh) __attribute__((always_inline)) {
@@ -332,17 +287,15 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
         const uint2 hi4 = read_tr16(vt_base + voff[mh] + 16 * ROWB);
         return make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
       };
-      uint4 vt[QLDS ? 1 : MH];
-      if constexpr (!QLDS) {
+      uint4 vt[MH];
 #pragma unroll
-        for (int mh = 0; mh < MH; ++mh) vt[mh] = read_v(mh);
-        if (cs.x + 1 < part.hi) read_k(1);
-      }
+      for (int mh = 0; mh < MH; ++mh) vt[mh] = read_v(mh);
+      if (cs.x + 1 < part.hi) read_k(1);
 
       // ---- O^T += V^T . P^T
 #pragma unroll
       for (int mh = 0; mh < MH; ++mh) {
-        const uint4 v = QLDS ? read_v(mh) : vt[QLDS ? 0 : mh];
+        const uint4 v = vt[mh];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           ot[mh][nb] = mfma16<BF>(v, phi[nb], ot[mh][nb]);
@@ -366,7 +319,6 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
       if (lane == 0) s_bad[wave] = anybad != 0ull;
     }
     // ---- fold the four waves into one state in LDS, one wave at a time
-    if constexpr (QLDS) __syncthreads();  // every wave is done with its slots
     for (int w = 0; w < WAVES; ++w) {
       if (wave == w) {
 #pragma unroll
@@ -433,10 +385,10 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
 
 // ---------------------------------------------------------------- launch
 
-template <bool BF, int H, int NB, bool PAGED, bool MASKED, bool QLDS>
-static hipError_t launch_mfma_q(const AttnArgs& a, hipStream_t stream) {
+template <bool BF, int H, int NB, bool PAGED, bool MASKED>
+static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int LDS_PER_CU = 160 * 1024;
-  const auto kern = attn_mfma_kernel<BF, H, NB, PAGED, MASKED, QLDS>;
+  const auto kern = attn_mfma_kernel<BF, H, NB, PAGED, MASKED>;
   static size_t static_lds = 0;
   static const hipError_t attr = [&] {
     hipFuncAttributes fa;
@@ -448,29 +400,14 @@ static hipError_t launch_mfma_q(const AttnArgs& a, hipStream_t stream) {
   }();
   if (attr != hipSuccess) return attr;
   const size_t pre = prefix_bytes(a.B);
-  int nslots = 2;
-  size_t shmem;
-  if constexpr (QLDS) {
-    shmem = pre + (size_t)NB * 16 * H * 2 + (size_t)WAVES * 2 * mfma_tile_bytes<H>();
-    if (static_lds + shmem > (size_t)LDS_PER_CU / 2) return hipErrorInvalidConfiguration;
-  } else {
-    // three slots per wave where the LDS allows (the prefix table grows with B)
-    const size_t slots3 = (size_t)WAVES * 3 * mfma_tile_bytes<H>();
-    nslots = static_lds + pre + slots3 <= (size_t)LDS_PER_CU ? 3 : 2;
-    shmem = pre + (size_t)WAVES * nslots * mfma_tile_bytes<H>();
-    if (static_lds + shmem > (size_t)LDS_PER_CU) return hipErrorInvalidConfiguration;
-  }
+  // three slots per wave where the LDS allows (the prefix table grows with B)
+  const size_t slots3 = (size_t)WAVES * 3 * mfma_tile_bytes<H>();
+  const int nslots = static_lds + pre + slots3 <= (size_t)LDS_PER_CU ? 3 : 2;
+  const size_t shmem = pre + (size_t)WAVES * nslots * mfma_tile_bytes<H>();
+  if (static_lds + shmem > (size_t)LDS_PER_CU) return hipErrorInvalidConfiguration;
   // one worker per workgroup
   hipLaunchKernelGGL(kern, dim3(a.W), dim3(THREADS), shmem, stream, a, nslots);
   return hipGetLastError();
-}
-
-template <bool BF, int H, int NB, bool PAGED, bool MASKED>
-static hipError_t launch_mfma_t(const AttnArgs& a, hipStream_t stream) {
-  if constexpr (H == 128 && NB <= 3) {
-    if (mfma_two_per_cu(a.B, H, NB * 16)) return launch_mfma_q<BF, H, NB, PAGED, MASKED, true>(a, stream);
-  }
-  return launch_mfma_q<BF, H, NB, PAGED, MASKED, false>(a, stream);
 }
 
 template <bool BF, int H, bool PAGED, bool MASKED>
@@ -501,7 +438,10 @@ static hipError_t launch_mfma_m(const AttnArgs& a, bool bf16, int H, bool paged,
 }
 
 int mfma_workgroups_per_cu(int B, int H, int RMAX) {
-  return H == 128 && mfma_two_per_cu(B, H, RMAX) ? 2 : 1;
+  (void)B;
+  (void)H;
+  (void)RMAX;
+  return 1;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream) {

@@ -30,7 +30,7 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream);
 // Workgroups of the vector-ALU kernel that fit one CU's LDS for B sequences.
 int valu_workgroups_per_cu(int B, int H);
-// Workgroups of the matrix-core kernel per CU for B sequences and RMAX rows.
+// Workgroups of the matrix-core kernel per CU (one: a wave per SIMD).
 int mfma_workgroups_per_cu(int B, int H, int RMAX);
 hipError_t launch_attn_mfma(const AttnArgs& a, bool bf16, int H, bool paged, hipStream_t stream);
 // Long query blocks: units of WIDE_ROWS rows whose four waves share each K/V tile.
