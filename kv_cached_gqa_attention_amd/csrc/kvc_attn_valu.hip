@@ -189,14 +189,27 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // ---- the K slot is free: the next step's K half goes there
       wait_lds();
       if (more) issue_k(cn);
+      // the lane groups' sums, one reduction step over every score at a time
+      // (the steps of one score depend on each other; those of different
+      // scores do not)
 #pragma unroll
       for (int i = 0; i < RPG; ++i)
 #pragma unroll
-        for (int r = 0; r < R; ++r) sc[r][i] = group_sum<LPR>(sc[r][i]) * a.scale_log2;
+        for (int r = 0; r < R; ++r) sc[r][i] += dpp_f<DPP_QUAD_XOR1>(sc[r][i]);
+#pragma unroll
+      for (int i = 0; i < RPG; ++i)
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[r][i] += dpp_f<DPP_QUAD_XOR2>(sc[r][i]);
+#pragma unroll
+      for (int i = 0; i < RPG; ++i)
+#pragma unroll
+        for (int r = 0; r < R; ++r) sc[r][i] = (sc[r][i] + dpp_f<DPP_ROW_HALF_MIRROR>(sc[r][i])) * a.scale_log2;
 
-      // ---- mask (only a unit's first and last tiles)
+      // ---- mask (only a unit's first and last tiles; the empty asm keeps
+      // the compiler from turning the branch into selects on every tile)
       const int tok0 = cs.tok0;
       if (tok0 + TILE > mask_hi || tok0 < mask_lo) {
+        asm volatile("");
 #pragma unroll
         for (int i = 0; i < RPG; ++i) {
           const int tok = tok0 + grp + GROUPS * i;
