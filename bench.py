@@ -50,8 +50,10 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # (the default timed region of the batched-decode step lasts over a second,
+    # long enough to resolve well under 1% and to show on a utilisation probe)
+    p.add_argument("--steps", type=int, default=10000)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="batched_decode_b64")
     p.add_argument("--ctx", type=int, default=4096, help="cached context for layers24_b1_sweep")
     p.add_argument("--num-workgroups", type=int, default=0)
