@@ -11,7 +11,7 @@ sum_b seq_len_b * 2 * K * H * elem_bytes. The default workload is batched
 decode (B=64, N=32, K=8, H=128, bf16, T=1, cached context U[512, 4096]).
 
 roofline: the attention kernel alone, timed with HIP events on the stream it
-is launched on: the median over 20 samples of 20 back-to-back launches, cache
+is launched on: the median over 20 samples of 100 back-to-back launches, cache
 replicas rotated so every launch reads from HBM rather than the 256 MB
 Infinity Cache. With the default workload the same kernel figures are also
 taken for the speculative-verify and paged long-context workloads
@@ -69,7 +69,7 @@ def parse():
                         "(auto: the verify and paged long-context workloads with the default "
                         "workload; none: no others)")
     p.add_argument("--samples", type=int, default=20, help="kernel timing samples (median)")
-    p.add_argument("--launches", type=int, default=20, help="back-to-back launches per sample")
+    p.add_argument("--launches", type=int, default=100, help="back-to-back launches per sample")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only copy a MIB-mebibyte device buffer 10 times (known-size reference "
                         "for the HBM byte counters) and print its bandwidth")
