@@ -340,7 +340,10 @@ kvc_status kvc_gather(const kvc_cache *paged, void *dst_k, void *dst_v, int B, i
  * range [lo, hi) of worker w, for every w < W (caller-owned, 2W entries)
  * and, when owners is not NULL, owners[x] for every x < total (caller-owned,
  * total entries): the worker the kernels take as holding step x when they
- * look up another worker's part of a unit. KVC_ERR_INVALID for total outside
+ * look up another worker's part of a unit. (The per-wave matrix-core
+ * kernel takes its equal shares of the steps plus a few virtual steps per
+ * unit, which it maps back to flat steps on the device; these are its ranges
+ * with none.) KVC_ERR_INVALID for total outside
  * [0, 2^32], W outside [1, 2^20], negative fast_workers or xcds, share
  * weights outside [1, 16], XCD factors outside [0, 64], or lo_hi NULL.
  */

@@ -89,6 +89,7 @@ struct Plan {
   int share_fast, share_slow;  // the shares' weights
   int xcd_even, xcd_odd;       // share factors by XCD parity (0: none)
   int xcds;     // workers numbered XCD by XCD (see worker_of), 0: in launch order
+  int seg_steps;  // virtual steps charged per unit entered (see make_partition)
   int workers;  // independent workers: waves (vector-ALU kernel) or workgroups (matrix cores)
   size_t off_o, off_ml, bytes;
 };
@@ -156,6 +157,16 @@ bool make_plan(int B, int T, int N, int K, int H, int max_seq_len, int num_wg, P
   p->xcd_even = xcds > 1 && xcds % 2 == 0 ? 16 : 0;
   p->xcd_odd = xcds > 1 && xcds % 2 == 0 ? 15 : 0;
   p->workers = p->W * per_wg;
+  // The per-wave matrix-core kernel pays for each unit a workgroup enters
+  // (the waves' fold, the partial's stores and count) about as much as for
+  // 1 + R/8 of its steps (one workgroup per CU, 40 rows: about 12 us a
+  // segment against 2.7 us a step; 64 rows with a draft tree: about 23
+  // against 3.2), so its shares are taken with that many virtual steps per
+  // unit (make_partition). The other kernels' segments cost too little
+  // against their steps for it to pay.
+  p->seg_steps = p->mfma && !p->wide ? 1 + p->R / 8 : 0;
+  // (that kernel takes equal shares in launch order: make_partition<true>)
+  if (p->mfma && !p->wide) p->fast = p->xcds = 0;
   const size_t slots = (size_t)p->workers + (size_t)p->units;
   p->off_ml = (size_t)COUNTER_SLOTS * sizeof(int32_t);
   p->off_o = p->off_ml + align_up(slots * p->RMAX * 2 * sizeof(float), 256);
@@ -322,6 +333,7 @@ kvc_status attn_common(const kvc_cache* c, const void* q, void* out, int out_dty
   a.xcd_even = p.xcd_even;
   a.xcd_odd = p.xcd_odd;
   a.xcds = p.xcds;
+  a.seg_steps = p.seg_steps;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.window = window;
   a.tree = tree;

@@ -41,6 +41,9 @@ constexpr int mfma_tile_bytes() { return TILE * H * 2; }
 // for a whole segment and the copies run on across unit boundaries. (A form
 // with two workgroups per CU, the query rows in LDS and the copies stopping
 // at each unit boundary, measured 1-4% slower on every verify shape.)
+// Each unit a workgroup enters costs it a fold, a partial and a count, so the
+// shares of the steps count a few virtual steps per unit (make_partition<true>):
+// a workgroup whose range enters more units gets fewer steps.
 template <bool BF, int H, int NB, bool PAGED, bool MASKED>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_mfma_kernel(AttnArgs a, int nslots) {
@@ -63,8 +66,9 @@ void attn_mfma_kernel(AttnArgs a, int nslots) {
 
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a, s_pre);
-  const int worker = worker_of(a, blockIdx.x);
-  const Partition part = make_partition(a, s_pre, worker);
+  // one workgroup per CU in launch order: equal shares, worker = workgroup
+  const int worker = blockIdx.x;
+  const Partition part = make_partition<true>(a, s_pre, worker);
   append_owned<H, THREADS, PAGED>(a, s_pre, part);
   if (part.lo >= part.hi) return;  // the whole workgroup: no barrier is skipped
 

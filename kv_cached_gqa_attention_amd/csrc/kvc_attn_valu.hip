@@ -71,7 +71,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a, s_pre);
   const int worker = worker_of(a, blockIdx.x);
-  const Partition part = make_partition(a, s_pre, worker);
+  const Partition part = make_partition<false>(a, s_pre, worker);
   append_owned<H, THREADS, PAGED>(a, s_pre, part);
   if (part.lo >= part.hi) return;  // the whole workgroup: no barrier is skipped
 

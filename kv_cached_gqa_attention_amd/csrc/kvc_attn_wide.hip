@@ -145,7 +145,7 @@ void attn_wide_kernel(AttnArgs a) {
   build_tile_prefix(a, s_pre, s_wave);
   fill_invalid<H>(a, s_pre);
   const int worker = worker_of(a, blockIdx.x);
-  const Partition part = make_partition(a, s_pre, worker);
+  const Partition part = make_partition<false>(a, s_pre, worker);
   append_owned<H, THREADS, PAGED>(a, s_pre, part);
   if (part.lo >= part.hi) return;  // the whole workgroup: no barrier is skipped
 

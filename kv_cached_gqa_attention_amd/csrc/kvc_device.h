@@ -90,6 +90,7 @@ struct AttnArgs {
   int32_t window;
   const uint32_t* tree;  // [B, T, tree_words]
   int32_t tree_words;    // mask words per new token: (T + 31) / 32
+  int32_t seg_steps;     // virtual steps charged per unit entered (see make_partition); 0: none
 };
 
 // ---------------------------------------------------------------- dtypes
@@ -421,6 +422,7 @@ struct Partition {
   int wf, ws;     // share weights of the older and the younger workgroup
   int xe, xo;     // share factors on even- and odd-numbered XCDs
   int64_t wt;     // sum of the shares (w_eff when equal)
+  int seg;        // virtual steps before each unit (see make_partition); 0: none
 
   // XCD factors of launch-order workers [0, n) (even ones xe, odd ones xo),
   // and its inverse: the largest n with xsum(n) <= v
@@ -501,6 +503,7 @@ __host__ __device__ inline Partition partition_of(int64_t total, int W, int fast
   }
   p.wf = share_fast;
   p.ws = share_slow;
+  p.seg = 0;
   // the XCD factors only with the weighted shares of a full round (an even
   // number of fast workers keeps the parity pattern of launch order)
   const bool xw = p.fast && xcd_even > 0 && xcd_odd > 0 && (p.per || p.fast % 2 == 0);
@@ -523,11 +526,68 @@ __host__ __device__ inline Partition partition_of(int64_t total, int W, int fast
   return p;
 }
 
+// The flat step a virtual step v stands for, with c = a.seg_steps > 0
+// virtual steps placed before each unit's steps: unit u ((b * K + k) * RB +
+// rb, in flat order) then starts at virtual step (its first flat step) +
+// c * u, and its c virtual steps stand for its first flat step.
+__device__ inline int64_t flat_of_virtual(const AttnArgs& a, const int32_t* s_pre, int64_t v) {
+  const int64_t c = a.seg_steps;
+  const int64_t cu = c * a.K * a.RB;  // virtual steps of one sequence's units
+  if (v >= (int64_t)s_pre[a.B] * a.K + cu * a.B) return (int64_t)s_pre[a.B] * a.K;
+  // last b whose virtual start s_pre[b] * K + cu * b is <= v
+  int lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)s_pre[mid] * a.K + cu * mid <= v) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int tk = s_pre[b + 1] - s_pre[b];
+  int64_t off = v - ((int64_t)s_pre[b] * a.K + cu * b);
+  const int64_t span = tk + c * a.RB;  // virtual steps of one (b, k)
+  const int64_t k = off / span;
+  off -= k * span;
+  int64_t flat = (int64_t)s_pre[b] * a.K + k * tk;
+  const int len = s_pre[a.B + 1 + b];
+  for (int rb = 0; rb < a.RB; ++rb) {
+    if (off < c) return flat;
+    off -= c;
+    const int us = unit_steps(a, len, rb);
+    if (off < us) return flat + off;
+    off -= us;
+    flat += us;
+  }
+  return flat;
+}
+
+// This worker's flat step range. With a.seg_steps = c > 0 the shares are
+// taken of the virtual steps (c before each unit: the fixed cost of a
+// segment, the waves' fold and the partial's stores, in steps), so a
+// worker whose range enters more units gets fewer real steps; the range is
+// the flat steps its virtual range stands for. Ranges stay contiguous and
+// cover every flat step once; a worker whose virtual range lies within one
+// unit's virtual steps gets none. Partition::owner takes virtual steps:
+// flat step x of unit u is virtual step x + c * (u + 1).
+// COSTED: equal shares with those virtual steps (the per-wave matrix-core
+// kernel, one workgroup per CU in launch order; the compiler folds the
+// equal shares into the owner lookups). Otherwise the launch's weighted
+// shares of the flat steps alone (a.seg_steps is not read).
+template <bool COSTED>
 __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int32_t* s_pre,
                                                     int w) {
   const int64_t total = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[a.B]) * a.K;
-  return partition_of(total, a.W, a.fast_workers, a.xcds, a.share_fast, a.share_slow, a.xcd_even,
-                      a.xcd_odd, w);
+  if constexpr (!COSTED) {
+    return partition_of(total, a.W, a.fast_workers, a.xcds, a.share_fast, a.share_slow,
+                        a.xcd_even, a.xcd_odd, w);
+  } else {
+    const int64_t virt = (int64_t)a.seg_steps * a.B * a.K * a.RB;
+    Partition p = partition_of(total + virt, a.W, 0, 0, 1, 1, 0, 0, w);
+    p.seg = a.seg_steps;
+    if (p.seg > 0) {
+      p.lo = flat_of_virtual(a, s_pre, p.lo);
+      p.hi = flat_of_virtual(a, s_pre, p.hi);
+    }
+    return p;
+  }
 }
 
 // Segment containing flat step x (x < p.total).
@@ -562,9 +622,9 @@ __device__ __forceinline__ Segment find_segment(const AttnArgs& a, const int32_t
   s.t_begin = __builtin_amdgcn_readfirstlane(off);
   const int64_t room = p.hi - x;
   s.t_end = (int64_t)(tb - s.t_begin) < room ? tb : s.t_begin + (int)room;
-  const int64_t ustart = x - s.t_begin;
-  s.first_wg = p.owner(ustart);
-  s.n_parts = p.owner(ustart + tb - 1) - s.first_wg + 1;
+  const int64_t vstart = x - s.t_begin + (int64_t)p.seg * (s.unit + 1);  // virtual
+  s.first_wg = p.owner(vstart);
+  s.n_parts = p.owner(vstart + tb - 1) - s.first_wg + 1;
   // step indices from here on count from the sequence's first token
   const int fs = unit_first_step(a, s.seq_len);
   s.t_begin += fs;
