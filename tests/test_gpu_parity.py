@@ -157,6 +157,19 @@ def test_any_workgroup_count_gives_the_same_function(gpu_device, nwg, T, N, K):
     compare_units(run, all_units(run.inp))
 
 
+# The matrix-core kernel's shares count 1 + R/8 virtual steps before each
+# unit (R query rows per unit). With units of one to a few 128-token steps,
+# fewer real steps than virtual ones, many workgroups' ranges hold only
+# virtual steps or a piece of one unit; the ranges must still cover every
+# step exactly once and the owner lookups must agree with them.
+@pytest.mark.parametrize("nwg", [0, 5, 64, 300, 1000])
+@pytest.mark.parametrize("T,N,K", [(5, 64, 8), (2, 32, 4)])
+def test_verify_shares_over_short_units(gpu_device, nwg, T, N, K):
+    prior = [0, 1, 3, 60, 122, 123, 124, 250, 251, 600, 1, 2000, 7, 300, 129, 5]
+    run = run_case(len(prior), T, N, K, 128, BF, prior, seed=91, num_workgroups=nwg)
+    compare_units(run, all_units(run.inp))
+
+
 @pytest.mark.parametrize("T,N,K", [(1, 32, 8), (5, 64, 8), (3, 6, 2)])
 def test_paged_equals_contiguous_bitwise(gpu_device, T, N, K):
     kw = dict(B=4, T=T, N=N, K=K, H=128, dtype=BF, prior=[1, 200, 1500, 64], seed=78,
