@@ -341,15 +341,32 @@ kvc_status kvc_gather(const kvc_cache *paged, void *dst_k, void *dst_v, int B, i
  * and, when owners is not NULL, owners[x] for every x < total (caller-owned,
  * total entries): the worker the kernels take as holding step x when they
  * look up another worker's part of a unit. (The per-wave matrix-core
- * kernel takes its equal shares of the steps plus a few virtual steps per
- * unit, which it maps back to flat steps on the device; these are its ranges
- * with none.) KVC_ERR_INVALID for total outside
+ * kernel's shares: kvc_partition_ranges_costed.) KVC_ERR_INVALID for total outside
  * [0, 2^32], W outside [1, 2^20], negative fast_workers or xcds, share
  * weights outside [1, 16], XCD factors outside [0, 64], or lo_hi NULL.
  */
 kvc_status kvc_partition_ranges(int64_t total, int W, int fast_workers, int xcds, int share_fast,
                                 int share_slow, int xcd_even, int xcd_odd, int64_t *lo_hi,
                                 int32_t *owners);
+
+/*
+ * Test export (host only, nothing is launched): the flat step ranges of the
+ * per-wave matrix-core kernel's costed partition, computed by the kernel's
+ * own code: equal shares over W workers of the flat steps plus seg_steps
+ * virtual steps placed before each unit, each worker's virtual range mapped
+ * back to the flat steps it stands for (a unit's virtual steps stand for its
+ * first flat step). Units are (b, k, rb) in that order, B sequences, K heads
+ * and RB row blocks each; unit (b, k, rb) has unit_steps[b * RB + rb] steps
+ * for every k (caller-owned, B * RB entries). Writes lo_hi[2w], lo_hi[2w + 1]
+ * for every w < W (caller-owned, 2W entries) and, when owners is not NULL,
+ * owners[x] for every flat step x (caller-owned, K times the sum of
+ * unit_steps entries): the worker the kernel takes as holding step x.
+ * KVC_ERR_INVALID for B outside [1, 2^16], K outside [1, 1024], RB outside
+ * [1, 64], a unit_steps entry outside [0, 2^20], more than 2^32 steps, W
+ * outside [1, 2^20], seg_steps outside [0, 64], or unit_steps or lo_hi NULL.
+ */
+kvc_status kvc_partition_ranges_costed(int B, int K, int RB, const int32_t *unit_steps, int W,
+                                       int seg_steps, int64_t *lo_hi, int32_t *owners);
 
 #ifdef __cplusplus
 }

@@ -40,6 +40,7 @@ EXPORTS = (
     "kvc_status_string",
     "kvc_gather",
     "kvc_partition_ranges",
+    "kvc_partition_ranges_costed",
 )
 
 
@@ -121,6 +122,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kvc_partition_ranges.argtypes = [ctypes.c_int64, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          vp, vp]
     lib.kvc_partition_ranges.restype = c_int
+    lib.kvc_partition_ranges_costed.argtypes = [c_int, c_int, c_int, vp, c_int, c_int, vp, vp]
+    lib.kvc_partition_ranges_costed.restype = c_int
     if path is None:
         _lib = lib
     return lib

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "kvc.h"
 #include "kvc_internal.h"
@@ -501,6 +502,42 @@ kvc_status kvc_partition_ranges(int64_t total, int W, int fast_workers, int xcds
     const kvc::Partition p = kvc::partition_of(total, W, fast_workers, xcds, share_fast, share_slow,
                                                xcd_even, xcd_odd, 0);
     for (int64_t x = 0; x < total; ++x) owners[x] = p.owner(x);
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_partition_ranges_costed(int B, int K, int RB, const int32_t* unit_steps, int W,
+                                       int seg_steps, int64_t* lo_hi, int32_t* owners) {
+  if (B < 1 || B > (1 << 16) || K < 1 || K > 1024 || RB < 1 || RB > 64 || !unit_steps || W < 1 ||
+      W > (1 << 20) || seg_steps < 0 || seg_steps > 64 || !lo_hi)
+    return KVC_ERR_INVALID;
+  std::vector<int32_t> pre((size_t)B + 1);
+  int64_t run = 0;
+  for (int b = 0; b < B; ++b) {
+    pre[b] = (int32_t)run;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int32_t n = unit_steps[(int64_t)b * RB + rb];
+      if (n < 0 || n > (1 << 20)) return KVC_ERR_INVALID;
+      run += n;
+    }
+    if (run * K > ((int64_t)1 << 32)) return KVC_ERR_INVALID;
+  }
+  pre[B] = (int32_t)run;
+  const int64_t total = run * K;
+  const auto us = [&](int b, int rb) { return unit_steps[(int64_t)b * RB + rb]; };
+  for (int w = 0; w < W; ++w) {
+    const kvc::Partition p = kvc::costed_partition(total, B, K, RB, seg_steps, pre.data(), us, W, w);
+    lo_hi[2 * w] = p.lo;
+    lo_hi[2 * w + 1] = p.hi;
+  }
+  if (owners && total > 0) {
+    // the lookup the kernel makes: flat step x of unit u at virtual x + c (u + 1)
+    const kvc::Partition p = kvc::costed_partition(total, B, K, RB, seg_steps, pre.data(), us, W, 0);
+    int64_t x = 0, u = 0;
+    for (int b = 0; b < B; ++b)
+      for (int k = 0; k < K; ++k)
+        for (int rb = 0; rb < RB; ++rb, ++u)
+          for (int i = 0; i < us(b, rb); ++i, ++x) owners[x] = p.owner(x + (int64_t)seg_steps * (u + 1));
   }
   return KVC_OK;
 }

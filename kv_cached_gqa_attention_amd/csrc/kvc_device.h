@@ -526,37 +526,54 @@ __host__ __device__ inline Partition partition_of(int64_t total, int W, int fast
   return p;
 }
 
-// The flat step a virtual step v stands for, with c = a.seg_steps > 0
-// virtual steps placed before each unit's steps: unit u ((b * K + k) * RB +
-// rb, in flat order) then starts at virtual step (its first flat step) +
-// c * u, and its c virtual steps stand for its first flat step.
-__device__ inline int64_t flat_of_virtual(const AttnArgs& a, const int32_t* s_pre, int64_t v) {
-  const int64_t c = a.seg_steps;
-  const int64_t cu = c * a.K * a.RB;  // virtual steps of one sequence's units
-  if (v >= (int64_t)s_pre[a.B] * a.K + cu * a.B) return (int64_t)s_pre[a.B] * a.K;
-  // last b whose virtual start s_pre[b] * K + cu * b is <= v
-  int lo = 0, hi = a.B - 1;
+// The flat step a virtual step v stands for, with c > 0 virtual steps
+// placed before each unit's steps: unit u ((b * K + k) * RB + rb, in flat
+// order) then starts at virtual step (its first flat step) + c * u, and its
+// c virtual steps stand for its first flat step. pre[b] (b <= B): the steps
+// of one (b', k) summed over b' < b; us(b, rb): the steps of unit (b, k, rb).
+template <typename UnitSteps>
+__host__ __device__ inline int64_t flat_of_virtual(int B, int K, int RB, int64_t c, const int32_t* pre,
+                                                   UnitSteps us, int64_t v) {
+  const int64_t cu = c * K * RB;  // virtual steps of one sequence's units
+  if (v >= (int64_t)pre[B] * K + cu * B) return (int64_t)pre[B] * K;
+  // last b whose virtual start pre[b] * K + cu * b is <= v
+  int lo = 0, hi = B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)s_pre[mid] * a.K + cu * mid <= v) lo = mid; else hi = mid - 1;
+    if ((int64_t)pre[mid] * K + cu * mid <= v) lo = mid; else hi = mid - 1;
   }
   const int b = lo;
-  const int tk = s_pre[b + 1] - s_pre[b];
-  int64_t off = v - ((int64_t)s_pre[b] * a.K + cu * b);
-  const int64_t span = tk + c * a.RB;  // virtual steps of one (b, k)
+  const int tk = pre[b + 1] - pre[b];
+  int64_t off = v - ((int64_t)pre[b] * K + cu * b);
+  const int64_t span = tk + c * RB;  // virtual steps of one (b, k)
   const int64_t k = off / span;
   off -= k * span;
-  int64_t flat = (int64_t)s_pre[b] * a.K + k * tk;
-  const int len = s_pre[a.B + 1 + b];
-  for (int rb = 0; rb < a.RB; ++rb) {
+  int64_t flat = (int64_t)pre[b] * K + k * tk;
+  for (int rb = 0; rb < RB; ++rb) {
     if (off < c) return flat;
     off -= c;
-    const int us = unit_steps(a, len, rb);
-    if (off < us) return flat + off;
-    off -= us;
-    flat += us;
+    const int n = us(b, rb);
+    if (off < n) return flat + off;
+    off -= n;
+    flat += n;
   }
   return flat;
+}
+
+// Worker w's partition of `total` flat steps over W workers in equal shares
+// of the steps plus c virtual steps before each of the B * K * RB units
+// (flat_of_virtual), its range mapped back to flat steps. Host-callable for
+// the checks of the test export.
+template <typename UnitSteps>
+__host__ __device__ inline Partition costed_partition(int64_t total, int B, int K, int RB, int c,
+                                                      const int32_t* pre, UnitSteps us, int W, int w) {
+  Partition p = partition_of(total + (int64_t)c * B * K * RB, W, 0, 0, 1, 1, 0, 0, w);
+  p.seg = c;
+  if (c > 0) {
+    p.lo = flat_of_virtual(B, K, RB, c, pre, us, p.lo);
+    p.hi = flat_of_virtual(B, K, RB, c, pre, us, p.hi);
+  }
+  return p;
 }
 
 // This worker's flat step range. With a.seg_steps = c > 0 the shares are
@@ -565,8 +582,8 @@ __device__ inline int64_t flat_of_virtual(const AttnArgs& a, const int32_t* s_pr
 // worker whose range enters more units gets fewer real steps; the range is
 // the flat steps its virtual range stands for. Ranges stay contiguous and
 // cover every flat step once; a worker whose virtual range lies within one
-// unit's virtual steps gets none. Partition::owner takes virtual steps:
-// flat step x of unit u is virtual step x + c * (u + 1).
+// unit's virtual steps gets none (costed_partition). Partition::owner takes
+// virtual steps: flat step x of unit u is virtual step x + c * (u + 1).
 // COSTED: equal shares with those virtual steps (the per-wave matrix-core
 // kernel, one workgroup per CU in launch order; the compiler folds the
 // equal shares into the owner lookups). Otherwise the launch's weighted
@@ -579,14 +596,8 @@ __device__ __forceinline__ Partition make_partition(const AttnArgs& a, const int
     return partition_of(total, a.W, a.fast_workers, a.xcds, a.share_fast, a.share_slow,
                         a.xcd_even, a.xcd_odd, w);
   } else {
-    const int64_t virt = (int64_t)a.seg_steps * a.B * a.K * a.RB;
-    Partition p = partition_of(total + virt, a.W, 0, 0, 1, 1, 0, 0, w);
-    p.seg = a.seg_steps;
-    if (p.seg > 0) {
-      p.lo = flat_of_virtual(a, s_pre, p.lo);
-      p.hi = flat_of_virtual(a, s_pre, p.hi);
-    }
-    return p;
+    const auto us = [&](int b, int rb) { return unit_steps(a, s_pre[a.B + 1 + b], rb); };
+    return costed_partition(total, a.B, a.K, a.RB, a.seg_steps, s_pre, us, a.W, w);
   }
 }
 

@@ -135,3 +135,105 @@ def test_rejects_bad_arguments(lib, bad):
                                   buf.ctypes.data_as(ctypes.c_void_p), None)
     assert st == -1  # KVC_ERR_INVALID
     assert lib.kvc_partition_ranges(10, 4, 0, 0, 5, 4, 0, 0, None, None) == -1
+
+
+# ---- the per-wave matrix-core kernel's costed shares
+#
+# Definition: lay the steps out unit by unit ((b, k, rb) in that order), each
+# unit's steps preceded by c virtual steps that stand for its first step;
+# split that list into equal shares (worker w: entries [n w / W', n (w+1) / W')
+# of n = len, W' = min(W, n)); a worker's range is [the flat step its first
+# entry stands for, the one its end entry stands for), the end of the list
+# standing for the last step + 1. Brute force below, on small inputs.
+
+def costed(lib, unit_steps, K, W, c):
+    B, RB = unit_steps.shape
+    total = int(unit_steps.sum()) * K
+    us = np.ascontiguousarray(unit_steps, dtype=np.int32)
+    lo_hi = np.zeros(2 * W, dtype=np.int64)
+    owners = np.full(max(total, 1), -1, dtype=np.int32)
+    st = lib.kvc_partition_ranges_costed(B, K, RB, us.ctypes.data_as(ctypes.c_void_p), W, c,
+                                         lo_hi.ctypes.data_as(ctypes.c_void_p),
+                                         owners.ctypes.data_as(ctypes.c_void_p))
+    assert st == 0
+    return lo_hi.reshape(W, 2), owners[:total]
+
+
+def costed_brute(unit_steps, K, W, c):
+    B, RB = unit_steps.shape
+    stands, real_pos = [], []  # per virtual entry: the flat step it stands for
+    flat = 0
+    for b in range(B):
+        for k in range(K):
+            for rb in range(RB):
+                n = int(unit_steps[b, rb])
+                stands += [flat] * c
+                for i in range(n):
+                    real_pos.append(len(stands))
+                    stands.append(flat + i)
+                flat += n
+    total, nv = flat, len(stands)
+    w_eff = min(W, nv)
+    at = lambda v: stands[v] if v < nv else total
+    r = np.zeros((W, 2), dtype=np.int64)
+    vb = [nv * w // w_eff for w in range(w_eff + 1)] if w_eff else [0]
+    for w in range(w_eff):
+        r[w] = (at(vb[w]), at(vb[w + 1]))
+    owners = np.array([max(w for w in range(w_eff) if vb[w] <= v) for v in real_pos], dtype=np.int32)
+    return r, owners
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("c", [0, 1, 3, 6, 9])
+def test_costed_shares_match_their_definition(lib, seed, c):
+    rng = np.random.default_rng(1000 + seed)
+    B, K, RB = int(rng.integers(1, 7)), int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    unit_steps = rng.integers(0, 6, size=(B, RB))
+    if seed % 3 == 0:
+        unit_steps[rng.random((B, RB)) < 0.4] = 0  # empty units (invalid lengths)
+    W = int(rng.choice([1, 2, 3, 7, 16, 50, 300]))
+    got, own = costed(lib, unit_steps, K, W, c)
+    want, want_own = costed_brute(unit_steps, K, W, c)
+    assert (got == want).all(), (got.tolist(), want.tolist())
+    assert (own == want_own).all()
+    # the plain properties: contiguous, covering, owners hold their steps
+    total = int(unit_steps.sum()) * K
+    nonempty = got[got[:, 1] > got[:, 0]]
+    if total:
+        assert nonempty[0, 0] == 0 and nonempty[-1, 1] == total
+        assert (nonempty[1:, 0] == nonempty[:-1, 1]).all()
+        for x in range(total):
+            assert got[own[x], 0] <= x < got[own[x], 1]
+
+
+def test_costed_shares_with_none_are_the_equal_shares(lib):
+    unit_steps = np.array([[40, 0], [7, 3], [100, 1]])
+    got, own = costed(lib, unit_steps, 3, 16, 0)
+    want, want_own = ranges(lib, int(unit_steps.sum()) * 3, 16)
+    assert (got == want).all() and (own == want_own).all()
+
+
+def test_costed_shares_give_fewer_steps_to_ranges_entering_more_units(lib):
+    # 64 one-step units then one unit of 448 steps, 16 workers, c = 6: every
+    # share is (64 * 7 + 448 + 6) / 16 = 56.4 virtual steps, so a worker over
+    # the short units holds ~8 real steps and one inside the long unit ~56
+    unit_steps = np.array([[1]] * 64 + [[448]])
+    got, _ = costed(lib, unit_steps, 1, 16, 6)
+    size = got[:, 1] - got[:, 0]
+    assert size.sum() == 512
+    assert size[:7].max() <= 9 and size[9:].min() >= 55
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=0), dict(B=(1 << 16) + 1), dict(K=0), dict(RB=0), dict(RB=65), dict(W=0),
+    dict(W=(1 << 20) + 1), dict(c=-1), dict(c=65), dict(steps=-1), dict(steps=(1 << 20) + 1),
+])
+def test_costed_rejects_bad_arguments(lib, bad):
+    a = dict(B=2, K=2, RB=1, W=4, c=3, steps=5)
+    a.update(bad)
+    us = np.full(max(a["B"], 1) * max(a["RB"], 1), a["steps"], dtype=np.int32)
+    buf = np.zeros(2 * max(a["W"], 1), dtype=np.int64)
+    st = lib.kvc_partition_ranges_costed(a["B"], a["K"], a["RB"], us.ctypes.data_as(ctypes.c_void_p), a["W"],
+                                         a["c"], buf.ctypes.data_as(ctypes.c_void_p), None)
+    assert st == -1  # KVC_ERR_INVALID
+    assert lib.kvc_partition_ranges_costed(2, 2, 1, None, 4, 3, buf.ctypes.data_as(ctypes.c_void_p), None) == -1
